@@ -1,0 +1,176 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 library: block quantizer,
+ * dequantizer, W4A16 decode GEMV and W4A4 GEMM.
+ *
+ * Format (from the pages "Tu pipeline NVFP4: meter 62 GB de modelo en 24 GB de
+ * laptop", section 2 "Que es realmente NVFP4", and "NVFP4 en difusion: la
+ * misma cuantizacion, un motor completamente distinto", section 2
+ * "NVFP4 sin vLLM: torch._scaled_mm a mano"):
+ *   - a tensor W [rows, cols] (row-major, cols = the reduction/input
+ *     dimension K) is cut into 16-element blocks along cols;
+ *   - each element is an E2M1 code (bit 3 sign, bits 2..1 exponent with
+ *     bias 1, bit 0 mantissa; values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their
+ *     negatives), packed two per byte: codes[r, i] = code(W[r, 2i]) |
+ *     code(W[r, 2i+1]) << 4  (low nibble = even column);
+ *   - each block has one FP8 E4M3 ("fn": bias 7, max 448, no infinities)
+ *     scale byte: scales[r, j] for elements j*16 .. j*16+15 of row r;
+ *   - the tensor has one fp32 second-level scale s_g;
+ *   - reconstruction: W^ = q * s_b * s_g.
+ * Encoding rules (the pages leave these open; this library fixes them):
+ *   - s_g = fp32(amax(|W|) / 2688), 2688 = 6 * 448 (1.0 for an all-zero
+ *     tensor), or a caller-given value;
+ *   - absmax block scale s_b = nearest E4M3 to amax_block / (6 s_g), exact
+ *     ties to the even code, saturating at 448;
+ *   - MSE block scale: the candidate with the least squared reconstruction
+ *     error among the E4M3 values c > 0 with a/2 <= c <= min(2a, 448)
+ *     (a = amax_block / (6 s_g)) plus the absmax scale; error summed in fp64,
+ *     element order, one rounding per operation; ties keep the smaller c;
+ *   - element code = nearest E2M1 value to W / (s_b s_g), exact ties to the
+ *     even code, saturating at 6; zero is always code 0 (never -0); all
+ *     codes are 0 when s_b = 0.
+ * Codes and scale bytes are bit-exact functions of the input.
+ *
+ * Conventions for every call:
+ *   - all pointers are DEVICE pointers (memory of the current HIP device),
+ *     row-major and contiguous; `stream` is a hipStream_t (NULL = default);
+ *   - calls are asynchronous on `stream`; the library never allocates,
+ *     frees or synchronizes the host in a call;
+ *   - the caller owns every buffer; inputs are never modified;
+ *   - arguments are validated before any launch; on error nothing is
+ *     launched and the status is returned;
+ *   - the fast path requires cols (K) % 32 == 0 and 16-byte aligned
+ *     pointers (4-byte for scales, global scale and 1-row outputs);
+ *     otherwise NVFP4_ERR_UNSUPPORTED / NVFP4_ERR_ALIGN is returned;
+ *   - non-finite inputs are a caller error: the outputs are unspecified.
+ */
+#ifndef NVFP4_H_
+#define NVFP4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_NULL = 1,        /* a required pointer is NULL */
+  NVFP4_ERR_SHAPE = 2,       /* negative size, or cols/K not a multiple of 16 */
+  NVFP4_ERR_ALIGN = 3,       /* pointer alignment below what the kernels load */
+  NVFP4_ERR_DTYPE = 4,       /* unknown dtype code */
+  NVFP4_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than nvfp4_workspace_bytes */
+  NVFP4_ERR_UNSUPPORTED = 6, /* valid NVFP4 shape outside the kernels' range (K % 32, M > 16, ...) */
+  NVFP4_ERR_LAUNCH = 7,      /* the HIP runtime reported an error at launch */
+  NVFP4_ERR_FLAGS = 8        /* unknown flag bits */
+} nvfp4_status;
+
+typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1 } nvfp4_dtype;
+
+/* flags for the quantizers (bit 0) */
+enum { NVFP4_GLOBAL_COMPUTE = 0, NVFP4_GLOBAL_GIVEN = 1 };
+
+/* operation ids for nvfp4_workspace_bytes */
+enum { NVFP4_OP_QUANTIZE = 0, NVFP4_OP_GEMM_W4A4 = 1 };
+
+/*
+ * nvfp4_quantize_absmax -- NVFP4 encoding with absmax block scales.
+ * ("Tu pipeline NVFP4 ...", section 2: absmax sets the block scale so that
+ * the largest magnitude lands on the top grid value, s = max|W_k| / 6.)
+ *   x            [rows, cols] input, dtype x_dtype (NVFP4_F32 or NVFP4_BF16)
+ *   codes        [rows, cols/2] uint8 output (two E2M1 codes per byte)
+ *   scales       [rows, cols/16] uint8 output (E4M3 bytes, 0x00..0x7E)
+ *   global_scale one fp32 on the device: written (s_g) with
+ *                NVFP4_GLOBAL_COMPUTE, read with NVFP4_GLOBAL_GIVEN
+ *                (must then be finite and > 0)
+ *   workspace    device scratch of >= nvfp4_workspace_bytes(NVFP4_OP_QUANTIZE,
+ *                rows, cols) bytes (may be NULL with NVFP4_GLOBAL_GIVEN);
+ *                holds per-workgroup amax partials; contents on return are
+ *                unspecified
+ * rows == 0 is a valid no-op (s_g = 1.0 is still written in COMPUTE mode).
+ */
+int nvfp4_quantize_absmax(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                          uint8_t* codes, uint8_t* scales, float* global_scale,
+                          int flags, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * nvfp4_quantize_mse -- NVFP4 encoding with MSE-searched block scales.
+ * ("Tu pipeline NVFP4 ...", section 2, box "Derivacion del objetivo de
+ * optimizacion MSE vs Absmax": s_b* = argmin over s_b of
+ * sum_k (W_k - s_b s_g Q(W_k / (s_b s_g)))^2; the algorithm table: "tries
+ * several scales and keeps the one that minimises the block's
+ * reconstruction error".)  Same arguments and layout as
+ * nvfp4_quantize_absmax; candidate set and arithmetic in the header comment.
+ * The chosen block error is never larger than the absmax scale's error.
+ */
+int nvfp4_quantize_mse(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                       uint8_t* codes, uint8_t* scales, float* global_scale,
+                       int flags, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * nvfp4_dequant -- W^ = q * s_b * s_g ("Tu pipeline NVFP4 ...", section 2,
+ * hierarchical reconstruction).  q * s_b is exact in fp32; the product with
+ * s_g is rounded once to fp32 (out_dtype NVFP4_F32) and that fp32 value is
+ * rounded to nearest-even bf16 for NVFP4_BF16.
+ *   codes [rows, cols/2], scales [rows, cols/16], global_scale: 1 device fp32
+ *   out   [rows, cols] of out_dtype
+ */
+int nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const float* global_scale,
+                  int64_t rows, int64_t cols, void* out, int out_dtype, void* stream);
+
+/*
+ * nvfp4_gemv_w4a16 -- weight-only decode product y = x W^T with NVFP4
+ * weights and bf16 activations ("Tu pipeline NVFP4 ...", section 2:
+ * W4A16 keeps the weights in 4 bits and unpacks them to 16 bits for the
+ * matmul; decoding reads every weight once per token and is bound by
+ * memory bandwidth).
+ *   y[m, n] = s_gW * sum_k x[m, k] * q[n, k] * s_b[n, k/16]
+ *   x        [M, K] bf16;  w_codes [N, K/2];  w_scales [N, K/16];
+ *   w_global 1 device fp32; y [M, N] of y_dtype (NVFP4_BF16 or NVFP4_F32)
+ *   1 <= M <= 16 (the decode batch); fp32 accumulation, fp32 epilogue,
+ *   round-to-nearest-even bf16 output.
+ */
+int nvfp4_gemv_w4a16(const void* x, const uint8_t* w_codes, const uint8_t* w_scales,
+                     const float* w_global, int64_t M, int64_t N, int64_t K,
+                     void* y, int y_dtype, void* stream);
+
+/*
+ * nvfp4_gemm_w4a4 -- y = A^ W^^T with the activation quantized to NVFP4 on
+ * every call ("NVFP4 en difusion ...", section 2: out = (A s_a)(B s_b)^T with
+ * bf16 output; the activation is quantized dynamically, 16-element block by
+ * 16-element block, on each call, with the same absmax criterion).
+ *   a        [M, K] bf16 activations
+ *   a_global NULL: s_gA = fp32(amax(|A|) / 2688) computed on the device;
+ *            otherwise a device fp32 used as s_gA (a static activation scale)
+ *   w_codes [N, K/2], w_scales [N, K/16], w_global: the NVFP4 weight
+ *   y        [M, N] of y_dtype (NVFP4_BF16 or NVFP4_F32)
+ *   workspace >= nvfp4_workspace_bytes(NVFP4_OP_GEMM_W4A4, M, K) bytes,
+ *            256-byte aligned.  On return it holds, at fixed offsets:
+ *              [0, 4)       s_gA (fp32)
+ *              [256, 256 + 2*M*K)  A^ / s_gA = q_a * s_a as fp16 [M, K]
+ *                           (exact: <= 6 significant bits, magnitudes in
+ *                           [2^-10, 2688]), i.e. the quantized activation
+ *              after that   amax partials (unspecified)
+ *   y[m, n] = round(fp32(s_gA * s_gW) * sum_k (q_a s_a)[m,k] (q_w s_w)[n,k])
+ *   with the products exact and the sum accumulated in fp32.
+ */
+int nvfp4_gemm_w4a4(const void* a, const float* a_global, const uint8_t* w_codes,
+                    const uint8_t* w_scales, const float* w_global,
+                    int64_t M, int64_t N, int64_t K, void* y, int y_dtype,
+                    void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace size in bytes for an operation (NVFP4_OP_QUANTIZE with
+ * (rows, cols), NVFP4_OP_GEMM_W4A4 with (M, K)); 0 for an unknown op. */
+size_t nvfp4_workspace_bytes(int op, int64_t rows_or_m, int64_t cols_or_k);
+
+/* Static, NUL-terminated description of a status code. */
+const char* nvfp4_status_string(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int nvfp4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H_ */

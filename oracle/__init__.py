@@ -1,0 +1,208 @@
+"""NVFP4 reference oracle -- TEST INFRASTRUCTURE ONLY.
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may
+import this package.  The GPU library never imports, links or calls it, and
+this package never touches the GPU library.  It wraps the plain C oracle
+(nvfp4_oracle.c, fp64, no FMA contraction) with numpy marshalling only:
+every numeric decision is taken in the C code.  `exact.py` is a second,
+independent checker in exact rational arithmetic for tiny inputs.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+ABSMAX = 0
+MSE = 1
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(
+            os.path.join(_HERE, "nvfp4_oracle.c")):
+        from . import build_oracle
+        build_oracle.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    lib.oracle_e2m1_value.restype = ctypes.c_double
+    lib.oracle_e2m1_value.argtypes = [ctypes.c_int]
+    lib.oracle_e4m3_value.restype = ctypes.c_double
+    lib.oracle_e4m3_value.argtypes = [ctypes.c_int]
+    lib.oracle_e4m3_nearest.restype = ctypes.c_int
+    lib.oracle_e4m3_nearest.argtypes = [ctypes.c_double]
+    lib.oracle_e2m1_nearest.restype = ctypes.c_int
+    lib.oracle_e2m1_nearest.argtypes = [ctypes.c_double]
+    lib.oracle_amax.restype = ctypes.c_float
+    lib.oracle_amax.argtypes = [P, i64]
+    lib.oracle_global_scale.restype = ctypes.c_float
+    lib.oracle_global_scale.argtypes = [ctypes.c_float]
+    lib.oracle_absmax_scale_code.restype = ctypes.c_int
+    lib.oracle_absmax_scale_code.argtypes = [P, ctypes.c_float]
+    lib.oracle_mse_scale_code.restype = ctypes.c_int
+    lib.oracle_mse_scale_code.argtypes = [P, ctypes.c_float]
+    lib.oracle_block_error.restype = ctypes.c_double
+    lib.oracle_block_error.argtypes = [P, ctypes.c_float, ctypes.c_int]
+    lib.oracle_quantize.restype = ctypes.c_int
+    lib.oracle_quantize.argtypes = [ctypes.c_int, P, i64, i64, ctypes.c_int, P, P, P, ctypes.c_int]
+    lib.oracle_dequant.restype = ctypes.c_int
+    lib.oracle_dequant.argtypes = [P, P, ctypes.c_float, i64, i64, P]
+    lib.oracle_dot_w4a16.restype = ctypes.c_int
+    lib.oracle_dot_w4a16.argtypes = [P, P, P, ctypes.c_float, i64, P, P, i64, P, P, ctypes.c_int]
+    lib.oracle_dot_w4a4.restype = ctypes.c_int
+    lib.oracle_dot_w4a4.argtypes = [P, P, ctypes.c_float, P, P, ctypes.c_float, i64, P, P, i64, P, P,
+                                    ctypes.c_int]
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _threads(threads):
+    if threads is None:
+        return len(os.sched_getaffinity(0))
+    return int(threads)
+
+
+def e2m1_value(code):
+    return _load().oracle_e2m1_value(int(code))
+
+
+def e4m3_value(byte):
+    return _load().oracle_e4m3_value(int(byte))
+
+
+def e4m3_nearest(a):
+    return _load().oracle_e4m3_nearest(float(a))
+
+
+def e2m1_nearest(x):
+    return _load().oracle_e2m1_nearest(float(x))
+
+
+def global_scale(amax):
+    return float(np.float32(_load().oracle_global_scale(float(np.float32(amax)))))
+
+
+def _as_f32_2d(x):
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim == 1:
+        x = x.reshape(1, -1)
+    return x
+
+
+def absmax_scale_code(block, sg):
+    b = np.ascontiguousarray(block, dtype=np.float32).reshape(16)
+    return _load().oracle_absmax_scale_code(_ptr(b), float(np.float32(sg)))
+
+
+def mse_scale_code(block, sg):
+    b = np.ascontiguousarray(block, dtype=np.float32).reshape(16)
+    return _load().oracle_mse_scale_code(_ptr(b), float(np.float32(sg)))
+
+
+def block_error(block, sg, scale_code):
+    b = np.ascontiguousarray(block, dtype=np.float32).reshape(16)
+    return _load().oracle_block_error(_ptr(b), float(np.float32(sg)), int(scale_code))
+
+
+def quantize(x, method=ABSMAX, sg=None, threads=None):
+    """Quantize a [rows, cols] float32 array (bf16 data widened to fp32).
+
+    Returns (codes uint8 [rows, cols/2], scales uint8 [rows, cols/16], sg float).
+    sg=None computes the per-tensor scale; a number uses it as given.
+    """
+    x = _as_f32_2d(x)
+    rows, cols = x.shape
+    codes = np.zeros((rows, cols // 2), dtype=np.uint8)
+    scales = np.zeros((rows, cols // 16), dtype=np.uint8)
+    sgv = np.zeros(1, dtype=np.float32)
+    given = sg is not None
+    if given:
+        sgv[0] = np.float32(sg)
+    rc = _load().oracle_quantize(int(method), _ptr(x), rows, cols, int(given), _ptr(sgv), _ptr(codes),
+                                 _ptr(scales), _threads(threads))
+    if rc != 0:
+        raise ValueError("oracle_quantize: bad shape %r" % (x.shape,))
+    return codes, scales, float(sgv[0])
+
+
+def dequant(codes, scales, sg, rows, cols):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    out = np.zeros((rows, cols), dtype=np.float32)
+    rc = _load().oracle_dequant(_ptr(codes), _ptr(scales), float(np.float32(sg)), rows, cols, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_dequant: bad shape")
+    return out
+
+
+def _pairs(M, N, pairs):
+    if pairs is None:
+        pm, pn = np.meshgrid(np.arange(M, dtype=np.int64), np.arange(N, dtype=np.int64), indexing="ij")
+        return pm.reshape(-1).copy(), pn.reshape(-1).copy()
+    pm = np.ascontiguousarray(pairs[0], dtype=np.int64)
+    pn = np.ascontiguousarray(pairs[1], dtype=np.int64)
+    return pm, pn
+
+
+def dot_w4a16(x, w_codes, w_scales, sgw, pairs=None, N=None, threads=None):
+    """fp64 y*[m,n] and tau for the requested (m, n) pairs (all pairs if None)."""
+    x = _as_f32_2d(x)
+    M, K = x.shape
+    if N is None:
+        N = w_scales.shape[0]
+    pm, pn = _pairs(M, N, pairs)
+    y = np.zeros(pm.shape[0], dtype=np.float64)
+    tau = np.zeros(pm.shape[0], dtype=np.float64)
+    wc = np.ascontiguousarray(w_codes, dtype=np.uint8)
+    ws = np.ascontiguousarray(w_scales, dtype=np.uint8)
+    rc = _load().oracle_dot_w4a16(_ptr(x), _ptr(wc), _ptr(ws), float(np.float32(sgw)), K, _ptr(pm), _ptr(pn),
+                                  pm.shape[0], _ptr(y), _ptr(tau), _threads(threads))
+    if rc != 0:
+        raise ValueError("oracle_dot_w4a16: bad shape")
+    return y, tau
+
+
+def dot_w4a4(a_codes, a_scales, sga, w_codes, w_scales, sgw, K, pairs=None, M=None, N=None, threads=None):
+    """fp64 y*[m,n] and tau for NVFP4 x NVFP4 operands (all pairs if None)."""
+    if M is None:
+        M = a_scales.shape[0]
+    if N is None:
+        N = w_scales.shape[0]
+    pm, pn = _pairs(M, N, pairs)
+    y = np.zeros(pm.shape[0], dtype=np.float64)
+    tau = np.zeros(pm.shape[0], dtype=np.float64)
+    ac = np.ascontiguousarray(a_codes, dtype=np.uint8)
+    as_ = np.ascontiguousarray(a_scales, dtype=np.uint8)
+    wc = np.ascontiguousarray(w_codes, dtype=np.uint8)
+    ws = np.ascontiguousarray(w_scales, dtype=np.uint8)
+    rc = _load().oracle_dot_w4a4(_ptr(ac), _ptr(as_), float(np.float32(sga)), _ptr(wc), _ptr(ws),
+                                 float(np.float32(sgw)), K, _ptr(pm), _ptr(pn), pm.shape[0], _ptr(y), _ptr(tau),
+                                 _threads(threads))
+    if rc != 0:
+        raise ValueError("oracle_dot_w4a4: bad shape")
+    return y, tau
+
+
+def bf16_rne_from_f64(v):
+    """Round fp64 values to the nearest bfloat16 value (ties to even), exactly,
+    returned as fp64.  Used for the output bracket of a bf16 GEMM result."""
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)                      # v = m * 2^e, 0.5 <= |m| < 1
+    e = np.maximum(e, -125)                 # bf16 subnormal spacing 2^-133
+    scaled = np.ldexp(v, 8 - e)             # 8 significant bits kept
+    return np.ldexp(np.rint(scaled), e - 8)
+
+
+def bracket_bf16(y, tau):
+    """Pass interval [bf16(y*-tau), bf16(y*+tau)] for a bf16 output."""
+    return bf16_rne_from_f64(np.asarray(y) - np.asarray(tau)), bf16_rne_from_f64(np.asarray(y) + np.asarray(tau))

@@ -1,0 +1,323 @@
+"""Pins for the CPU oracle against what the pages and mathematics fix.
+
+Every test here runs without a GPU.  The oracle is never compared with itself:
+each check uses the pages' printed values (tests/golden/), a library routine
+(torch's float8_e4m3fn / bfloat16 casts, numpy float64 matmul), an independent
+exact-rational implementation (oracle/exact.py), closed forms or invariants.
+"""
+import math
+import os
+from fractions import Fraction as F
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import exact
+from dit_quantization_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+# ---------------------------------------------------------------- formats
+
+def test_e2m1_decode_matches_page_grid():
+    for code, val in _read("e2m1_grid.txt"):
+        got = oracle.e2m1_value(int(code))
+        assert got == float(val) and math.copysign(1, got) == math.copysign(1, float(val)), code
+    distinct = {abs(oracle.e2m1_value(c)) for c in range(16)}
+    assert sorted(distinct) == [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+
+
+def test_e4m3_decode_matches_torch_all_bytes():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for b in range(256):
+        got = oracle.e4m3_value(b)
+        if math.isnan(ref[b]):
+            assert math.isnan(got), b
+        else:
+            assert got == ref[b], b
+    assert oracle.e4m3_value(0x7E) == 448.0 and oracle.e4m3_value(0x01) == 2.0 ** -9
+
+
+def test_e4m3_nearest_matches_torch_cast():
+    g = inputs.rng(123)
+    vals = list(g.uniform(0, 460, 4000)) + list(np.exp(g.uniform(-16, 6, 4000)))
+    # every midpoint between adjacent E4M3 values, and its fp32 neighbours
+    e4 = [oracle.e4m3_value(c) for c in range(127)]
+    for lo, hi in zip(e4[:-1], e4[1:]):
+        m = np.float32((lo + hi) / 2)
+        vals += [m, np.nextafter(m, np.float32(0)), np.nextafter(m, np.float32(1e9))]
+    vals = np.array(vals, dtype=np.float32)
+    vals = vals[vals <= 448.0]
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3_nearest(float(v)) for v in vals])
+    assert np.array_equal(got, ref)
+
+
+def test_e4m3_nearest_saturates():
+    for v in (448.0, 463.9, 464.0, 480.0, 1e6, 1e300):
+        assert oracle.e4m3_nearest(v) == 0x7E
+
+
+def test_e4m3_nearest_matches_exact_rounding():
+    g = inputs.rng(7)
+    for v in list(np.exp(g.uniform(-12, 7, 3000))) + [2.0 ** -10, 3 * 2.0 ** -11, 2.0 ** -11]:
+        want = exact.round_format(F(float(v)), 3, -6, exact.E4M3_MAX)
+        assert oracle.e4m3_value(oracle.e4m3_nearest(float(v))) == float(want), v
+
+
+def test_e2m1_nearest_ties_and_neighbours_exact():
+    pts = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.5, 1.0, 6.0, 7.0, 100.0, 0.0]
+    xs = []
+    for p in pts:
+        xs += [p, -p, np.nextafter(p, 0), np.nextafter(p, 1e9), -np.nextafter(p, 0), -np.nextafter(p, 1e9)]
+    xs += list(inputs.rng(5).uniform(-8, 8, 5000))
+    for x in xs:
+        want = exact.e2m1_code(exact.round_format(F(float(x)), 1, 0, exact.E2M1_MAX))
+        assert oracle.e2m1_nearest(float(x)) == want, x
+    # printed tie rule: 0.25->0, 0.75->1, 1.25->1, 1.75->2, 2.5->2, 3.5->4, 5->4
+    for x, v in [(0.25, 0), (0.75, 1), (1.25, 1), (1.75, 2), (2.5, 2), (3.5, 4), (5.0, 4)]:
+        assert oracle.e2m1_value(oracle.e2m1_nearest(x)) == v
+        assert oracle.e2m1_value(oracle.e2m1_nearest(-x)) == -v
+    assert oracle.e2m1_nearest(-0.1) == 0  # canonical +0
+
+
+def test_bf16_rounding_helper_matches_torch():
+    g = inputs.rng(9)
+    v = np.concatenate([g.standard_normal(20000), g.standard_normal(2000) * 1e-30, np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8])])
+    v32 = v.astype(np.float32)
+    ref = torch.from_numpy(v32).to(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.bf16_rne_from_f64(v32.astype(np.float64))
+    assert np.array_equal(got, ref)
+
+
+# ---------------------------------------------------------------- global scale
+
+def test_global_scale_exact():
+    g = inputs.rng(11)
+    for amax in list(g.uniform(0, 10, 2000).astype(np.float32)) + [np.float32(2688.0), np.float32(1e-38)]:
+        want = exact.global_scale(F(float(amax)))
+        assert oracle.global_scale(float(amax)) == float(want), amax
+    assert oracle.global_scale(0.0) == 1.0
+
+
+# ---------------------------------------------------------------- quantizer
+
+def _blocks_tiny(seed, n):
+    g = inputs.rng(seed)
+    out = []
+    for i in range(n):
+        kind = i % 4
+        if kind == 0:
+            b = g.standard_normal(16) * 0.02
+        elif kind == 1:
+            b = g.standard_t(5, 16) * 0.02
+        elif kind == 2:
+            b = g.standard_normal(16) * 0.02
+            b[0] *= (1, 3, 6, 12, 30)[i % 5]      # outlier factors of the toy experiment
+        else:
+            b = np.exp(g.uniform(-30, 5, 16)) * g.choice([-1, 1], 16)
+        out.append(b.astype(np.float32))
+    return np.stack(out)
+
+
+def test_quantize_absmax_matches_exact_rational():
+    x = _blocks_tiny(1, 96).reshape(6, 256)
+    codes, scales, sg = oracle.quantize(x, oracle.ABSMAX)
+    assert sg == float(exact.global_scale(F(float(np.abs(x).max()))))
+    for r in range(x.shape[0]):
+        for j in range(x.shape[1] // 16):
+            blk = [F(float(v)) for v in x[r, 16 * j:16 * j + 16]]
+            sb = exact.absmax_scale(blk, F(sg))
+            assert scales[r, j] == exact.E4M3_INDEX[sb]
+            cs = exact.codes_for(blk, sb, F(sg))
+            packed = [cs[2 * i] | (cs[2 * i + 1] << 4) for i in range(8)]
+            assert list(codes[r, 8 * j:8 * j + 8]) == packed
+
+
+def test_quantize_exact_ties_in_codes_and_scales():
+    # s_g = 1 given; blocks built so that W / s_b hits every E2M1 midpoint, and
+    # amax / 6 hits E4M3 midpoints exactly.
+    e4 = [oracle.e4m3_value(c) for c in range(127)]
+    rows = []
+    for c in (8, 20, 0x38, 60, 100, 125):
+        sb = e4[c]
+        mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+        row = [6 * sb] + [m * sb for m in mids] + [-m * sb for m in mids] + [0.0]
+        rows.append(row)
+    for lo, hi in zip(e4[1:-1:7], e4[2::7]):
+        mid = (lo + hi) / 2
+        rows.append([6 * mid] + [0.0] * 15)
+    x = np.array(rows, dtype=np.float32)
+    codes, scales, sg = oracle.quantize(x, oracle.ABSMAX, sg=1.0)
+    for r in range(x.shape[0]):
+        blk = [F(float(v)) for v in x[r]]
+        sb = exact.absmax_scale(blk, F(1))
+        assert scales[r, 0] == exact.E4M3_INDEX[sb]
+        cs = exact.codes_for(blk, sb, F(1))
+        assert list(codes[r]) == [cs[2 * i] | (cs[2 * i + 1] << 4) for i in range(8)]
+
+
+def test_pack_example_golden():
+    rows = {r[0]: r[1:] for r in _read("pack_example.txt")}
+    x = np.array([float(v) for v in rows["input"]], dtype=np.float32).reshape(1, 32)
+    codes, scales, _ = oracle.quantize(x, oracle.ABSMAX, sg=1.0)
+    assert [f"{b:02X}" for b in codes[0]] == rows["codes"]
+    assert [f"{b:02X}" for b in scales[0]] == rows["scales"]
+
+
+def test_mse_matches_exact_bruteforce_and_beats_absmax():
+    x = _blocks_tiny(2, 64)
+    sg = F(oracle.global_scale(float(np.abs(x).max())))
+    outside = 0
+    for blk_np in x:
+        blk = [F(float(v)) for v in blk_np]
+        best, best_err, gbest, gbest_err = exact.mse_search(blk, sg)
+        code = oracle.mse_scale_code(blk_np, float(sg))
+        chosen = exact.E4M3[code]
+        chosen_err = exact.block_error(blk, chosen, sg)
+        # oracle's fp64 choice is the exact windowed optimum (or an exact tie of it)
+        assert chosen_err == best_err or abs(chosen_err - best_err) <= best_err * F(1, 10 ** 12), (code, best)
+        # MSE never worse than absmax, exactly
+        abs_err = exact.block_error(blk, exact.absmax_scale(blk, sg), sg)
+        assert chosen_err <= abs_err
+        outside += gbest != best
+    # the unrestricted optimum is reported, not gated
+    print(f"blocks whose unrestricted optimum lies outside [a/2, 2a]: {outside}/{len(x)}")
+
+
+def test_mse_window_bounds_are_exact_e4m3_steps():
+    # a block whose a = amax/(6 s_g) is itself an E4M3 value: the window holds
+    # exactly 17 candidates (a/2 .. 2a inclusive) in the normal range.
+    blk = np.zeros(16, dtype=np.float32)
+    blk[0] = 6.0
+    a = 1.0
+    n = sum(1 for c in range(1, 127) if a / 2 <= oracle.e4m3_value(c) <= 2 * a)
+    assert n == 17
+    assert oracle.mse_scale_code(blk, 1.0) == 0x38  # exact representation wins (zero error)
+
+
+def test_worked_example_levels():
+    # s_b * s_g = 0.01 with s_g = 0.01 given and s_b = 1.0 (E4M3 0x38)
+    levels = sorted({float(r[0]) for r in _read("worked_example_scale_0p01.txt")})
+    codes = np.arange(16, dtype=np.uint8)
+    packed = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8).reshape(1, 8)
+    deq = oracle.dequant(packed, np.array([[0x38]], dtype=np.uint8), 0.01, 1, 16)[0]
+    got = sorted({float(v) for v in deq})
+    assert len(got) == len(levels) == 15
+    for g_, l_ in zip(got, levels):
+        assert abs(g_ - l_) <= 1e-7 * max(abs(l_), 1e-30)
+
+
+def test_roundtrip_of_representable_values():
+    g = inputs.rng(3)
+    e4 = [oracle.e4m3_value(c) for c in range(127)]
+    grid = [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+    rows = []
+    for _ in range(40):
+        c = int(g.integers(1, 127))
+        q = g.choice(grid, 16) * g.choice([-1, 1], 16)
+        q[int(g.integers(16))] = 6 * g.choice([-1, 1])
+        rows.append(q * e4[c])
+    x = np.array(rows, dtype=np.float32).reshape(-1, 16)
+    assert np.all(x == np.array(rows))         # values representable in fp32
+    codes, scales, _ = oracle.quantize(x, oracle.ABSMAX, sg=1.0)
+    back = oracle.dequant(codes, scales, 1.0, x.shape[0], 16)
+    assert np.array_equal(back, x)
+    codes_m, scales_m, _ = oracle.quantize(x, oracle.MSE, sg=1.0)
+    assert np.array_equal(oracle.dequant(codes_m, scales_m, 1.0, x.shape[0], 16), x)
+
+
+def test_memory_accounting_4p5_bits():
+    for params, bf16_gb, nv_gb, tol in _read("memory_accounting.txt"):
+        n = int(float(params))
+        rows, cols = 1, n  # the byte count depends only on the element count
+        nbytes = rows * cols // 2 + rows * cols // 16
+        assert abs(n * 2 / 1e9 - float(bf16_gb)) < 1e-9
+        assert abs(nbytes / 1e9 - float(nv_gb)) <= float(tol)
+        assert nbytes * 8 / n == 4.5
+    # the oracle's output layout: [R, C/2] codes + [R, C/16] scales
+    codes, scales, _ = oracle.quantize(np.ones((48, 160), np.float32))
+    total = codes.nbytes + scales.nbytes
+    assert total == 48 * 160 * (0.5 + 0.0625)
+    assert abs(scales.nbytes / total - 1 / 9) < 1e-12        # "11 %"
+
+
+# ---------------------------------------------------------------- products
+
+def test_dot_w4a16_one_hot_gives_dequant_row():
+    w = inputs.normal_f32((8, 64), 4, 0.02)
+    codes, scales, sg = oracle.quantize(w)
+    wh = oracle.dequant(codes, scales, sg, 8, 64).astype(np.float64)
+    x = np.eye(64, dtype=np.float32)[:5]
+    y, tau = oracle.dot_w4a16(x, codes, scales, sg)
+    y = y.reshape(5, 8)
+    # exact products: the one-hot picks W^[n, k] exactly (fp32-rounded dequant differs by < 1 ulp)
+    assert np.allclose(y, wh[:, :5].T, rtol=2 ** -23, atol=0)
+
+
+def test_dot_products_small_integer_exact_and_numpy_crosscheck():
+    g = inputs.rng(6)
+    K = 64
+    # operands whose NVFP4 encoding is exact (s_g = 1, scale 1.0 per block)
+    qa = g.choice([0, 0.5, 1, 1.5, 2, 3, 4, 6], (3, K)) * g.choice([-1, 1], (3, K))
+    qw = g.choice([0, 0.5, 1, 1.5, 2, 3, 4, 6], (5, K)) * g.choice([-1, 1], (5, K))
+    qa[:, ::16] = 6
+    qw[:, ::16] = -6
+    ac, as_, _ = oracle.quantize(qa.astype(np.float32), sg=1.0)
+    wc, ws, _ = oracle.quantize(qw.astype(np.float32), sg=1.0)
+    y, tau = oracle.dot_w4a4(ac, as_, 1.0, wc, ws, 1.0, K)
+    assert np.array_equal(y.reshape(3, 5), qa @ qw.T)          # exact small-integer result
+    y16, _ = oracle.dot_w4a16(qa.astype(np.float32), wc, ws, 1.0)
+    assert np.array_equal(y16.reshape(3, 5), qa @ qw.T)
+    # random operands: numpy float64 matmul of the dequantized operands
+    a = inputs.normal_f32((7, 256), 8)
+    w = inputs.student_t_f32((9, 256), 9)
+    ac, as_, sga = oracle.quantize(a)
+    wc, ws, sgw = oracle.quantize(w, oracle.MSE)
+    ah = oracle.dequant(ac, as_, sga, 7, 256).astype(np.float64)
+    whh = oracle.dequant(wc, ws, sgw, 9, 256).astype(np.float64)
+    y, tau = oracle.dot_w4a4(ac, as_, sga, wc, ws, sgw, 256)
+    ref = ah @ whh.T
+    assert np.allclose(y.reshape(7, 9), ref, rtol=0, atol=1e-6 * (np.abs(ah) @ np.abs(whh).T).max())
+    assert np.all(tau > 0)
+
+
+def test_tiny_config_end_to_end_is_consistent():
+    w, xb = inputs.tiny()
+    codes, scales, sg = oracle.quantize(w)
+    assert codes.shape == (256, 128) and scales.shape == (256, 16)
+    x = inputs.bf16_bits_to_f32(xb)
+    y, tau = oracle.dot_w4a16(x, codes, scales, sg)
+    wh = oracle.dequant(codes, scales, sg, 256, 256).astype(np.float64)
+    # fp32-rounded dequant vs exact: differences below 2^-23 * sum |x||w^|
+    assert np.all(np.abs(y - (x.astype(np.float64) @ wh.T)[0]) <= 2.0 ** -23 * (np.abs(x) @ np.abs(wh).T)[0])
+
+
+def test_mse_statistics_report():
+    """Parity unpinned (the page's ~0.70 x absmax and >25 % claims are narrative):
+    reported, not gated; only the invariant E(mse) <= E(absmax) is asserted."""
+    w = inputs.student_t_f32((64, 1024), 77)
+    ca, sa, sg = oracle.quantize(w, oracle.ABSMAX)
+    cm, sm, _ = oracle.quantize(w, oracle.MSE)
+    ea = (oracle.dequant(ca, sa, sg, 64, 1024).astype(np.float64) - w) ** 2
+    em = (oracle.dequant(cm, sm, sg, 64, 1024).astype(np.float64) - w) ** 2
+    ba = ea.reshape(-1, 16).sum(1)
+    bm = em.reshape(-1, 16).sum(1)
+    assert np.all(bm <= ba * (1 + 1e-6))
+    e4 = np.array([oracle.e4m3_value(c) for c in range(127)])
+    ratio = e4[sm.reshape(-1)] / np.maximum(e4[sa.reshape(-1)], 1e-30)
+    print(f"median s_mse/s_absmax = {np.median(ratio):.3f}; noise variance reduction = "
+          f"{1 - em.sum() / ea.sum():.3f}; blocks improved = {(bm < ba).mean():.3f}")
