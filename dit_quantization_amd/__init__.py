@@ -11,6 +11,6 @@ __all__ = ["inputs", "nvfp4"]
 
 def __getattr__(name):
     if name == "nvfp4":
-        from . import nvfp4 as mod
-        return mod
+        import importlib
+        return importlib.import_module(__name__ + ".nvfp4")
     raise AttributeError(name)

@@ -1,0 +1,277 @@
+// W4A4 GEMM with online NVFP4 activation quantization for gfx950.
+//
+// "NVFP4 en difusion: la misma cuantizacion, un motor completamente
+// distinto", section 2 ("NVFP4 sin vLLM: torch._scaled_mm a mano"): the
+// activation is quantized to NVFP4 on every call, 16-element block by block
+// with the absmax criterion, and out = (A s_a)(B s_b)^T is returned in 16-bit
+// precision (a "4-bit island with BF16 shores").
+//
+// Design (gfx950):
+//  * act_quant: absmax NVFP4 quantization of A (same encoder as the weight
+//    quantizer), written out as the exact fp16 values q_a * s_a (<= 6
+//    significant bits, magnitudes in [2^-10, 2688], so fp16 holds them
+//    exactly and the bf16/fp16 matrix cores can consume them directly).
+//  * gemm: 256x256 (or 128x128) output tiles per workgroup of 4 waves in a
+//    2x2 arrangement, K step 64.  A^ tiles go global -> registers -> LDS
+//    (XOR-swizzled 16-byte chunks, double buffered).  Packed weights go
+//    global -> registers; each lane unpacks its 32 codes with the hardware
+//    FP4 converter and one packed fp16 multiply by the block scale, giving
+//    exact fp16 q_w * s_w operands.  v_mfma_f32_32x32x16_f16 accumulates in
+//    fp32 (every product is exact); the epilogue multiplies by
+//    fp32(s_gA * s_gW) and rounds to bf16.
+//  * The k order inside each 64-wide K step is permuted identically for A
+//    and W (lane group g of an MFMA feeds k = 32 g + 8 s + j at sub-step s),
+//    which lets every lane read 16 contiguous bytes of packed weights.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace nvfp4 {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------- act quant
+
+// One lane per half block of the bf16 activation; lanes 2b, 2b+1 share block b.
+__global__ __launch_bounds__(256) void act_quant_f16_kernel(const u32x4* __restrict__ a, int64_t n_half,
+                                                            const float* __restrict__ sg_ptr,
+                                                            u32x4* __restrict__ a_hat) {
+  const float sg = *sg_ptr;
+  const float inv_sg = 1.0f / sg;
+  const double six_sg = 6.0 * (double)sg;
+  int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; h < n_half; h += stride) {
+    u32x4 v = __builtin_nontemporal_load(&a[h]);
+    float w[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w[2 * j] = bf16_bits_to_f32(v[j] & 0xFFFFu);
+      w[2 * j + 1] = bf16_bits_to_f32(v[j] >> 16);
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(w[j]));
+    m = fmaxf(m, __shfl_xor(m, 1));
+    uint32_t sc = e4m3_code_rne((double)m / six_sg);
+    float sb = e4m3_to_f32(sc);
+    uint32_t codes = encode8(w, sb, sg, inv_sg);
+    _Float16 sbh = (_Float16)sb;
+    f16x2 s2 = {sbh, sbh};
+    f16x2 q[4];
+    fp4x8_to_f16x2(codes, q);
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = __builtin_bit_cast(uint32_t, q[j] * s2);
+    a_hat[h] = o;
+  }
+}
+
+hipError_t launch_act_quant_f16(const uint16_t* a, int64_t n_elems, const float* sg, uint16_t* a_hat,
+                                hipStream_t stream) {
+  int64_t n_half = n_elems / 8;
+  if (n_half == 0) return hipSuccess;
+  int64_t wg = (n_half + 255) / 256;
+  if (wg > 8192) wg = 8192;
+  hipLaunchKernelGGL(act_quant_f16_kernel, dim3((unsigned)wg), dim3(256), 0, stream,
+                     reinterpret_cast<const u32x4*>(a), n_half, sg, reinterpret_cast<u32x4*>(a_hat));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- GEMM
+
+namespace {
+constexpr int BK = 64;  // K step (4 blocks of 16)
+}
+
+// Unpack 8 codes (one dword) into 8 exact fp16 values q * s_b.
+__device__ __forceinline__ f16x8 unpack8_f16(uint32_t c, f16x2 s2) {
+  f16x2 q[4];
+  fp4x8_to_f16x2(c, q);
+  f16x8 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f16x2 p = q[j] * s2;
+    r[2 * j] = p.x;
+    r[2 * j + 1] = p.y;
+  }
+  return r;
+}
+
+__device__ __forceinline__ f16x2 e4m3_to_f16x2(uint32_t b) {
+  _Float16 h = (_Float16)e4m3_to_f32(b);
+  return f16x2{h, h};
+}
+
+// BM x BN tile per workgroup, 4 waves in 2x2; each wave (BM/2) x (BN/2) as
+// TM x TN tiles of 32x32.  grid.x enumerates tiles (XCD-aware order).
+template <int BM, int BN>
+__global__ __launch_bounds__(256, 1) void gemm_w4a4_kernel(const uint16_t* __restrict__ a_hat,
+                                                           const float* __restrict__ sga_ptr,
+                                                           const uint8_t* __restrict__ codes,
+                                                           const uint8_t* __restrict__ scales,
+                                                           const float* __restrict__ sgw_ptr, int M, int N, int K,
+                                                           void* __restrict__ y, int bf16_out) {
+  constexpr int TM = BM / 64, TN = BN / 64;              // 32x32 tiles per wave
+  constexpr int A_CHUNKS = BM * BK * 2 / 16;             // 16-byte chunks per A tile
+  constexpr int A_PER_THREAD = A_CHUNKS / 256;
+  __shared__ __attribute__((aligned(16))) u32x4 lds_a[2][A_CHUNKS];
+
+  // Tile coordinates.  Consecutive workgroup ids go to different XCDs
+  // (round robin over 8); remap so that each XCD receives a contiguous run
+  // of tiles, which then share A rows / W rows in that XCD's L2.
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int ntiles = tiles_m * tiles_n;
+  int bid = blockIdx.x;
+  if ((ntiles & 7) == 0) {  // a bijection on [0, ntiles) when 8 divides it
+    const int per_xcd = ntiles >> 3;
+    bid = (bid & 7) * per_xcd + (bid >> 3);
+  }
+  // Walk tiles in groups of 8 M-tiles so neighbouring workgroups reuse W.
+  constexpr int GROUP = 8;
+  const int group = bid / (GROUP * tiles_n);
+  const int first_m = group * GROUP;
+  const int gsize = min(tiles_m - first_m, GROUP);
+  const int tm = first_m + (bid % (GROUP * tiles_n)) % gsize;
+  const int tn = (bid % (GROUP * tiles_n)) / gsize;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, g = lane >> 5;  // MFMA row/col and k lane group
+
+  // ---- A global -> LDS mapping: chunk i = tid + 256 j -> row i / 8, chunk i % 8
+  const u32x4* a_rows[A_PER_THREAD];
+#pragma unroll
+  for (int j = 0; j < A_PER_THREAD; ++j) {
+    int i = tid + 256 * j;
+    int r = i >> 3, c = i & 7;
+    int gr = min(m0 + r, M - 1);
+    a_rows[j] = reinterpret_cast<const u32x4*>(a_hat + (int64_t)gr * K) + c;
+  }
+  auto lds_slot = [](int r, int c) { return r * 8 + (c ^ (r & 7)); };
+
+  // ---- W rows of this lane: TN sub-tiles, row n0 + wn*(BN/2) + 32 t + l32
+  const uint8_t* wc[TN];
+  const uint8_t* wsc[TN];
+#pragma unroll
+  for (int t = 0; t < TN; ++t) {
+    int n = min(n0 + wn * (BN / 2) + 32 * t + l32, N - 1);
+    wc[t] = codes + (int64_t)n * (K / 2) + 16 * g;      // 32 codes = 16 bytes per K step
+    wsc[t] = scales + (int64_t)n * (K / 16) + 2 * g;    // 2 scale bytes per K step
+  }
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int t = 0; t < TN; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][t][r] = 0.0f;
+
+  const int KT = K / BK;
+  u32x4 areg[A_PER_THREAD];
+  u32x4 wreg[TN];
+  uint32_t sreg[TN];
+
+  // prologue: stage 0
+#pragma unroll
+  for (int j = 0; j < A_PER_THREAD; ++j) areg[j] = a_rows[j][0];
+#pragma unroll
+  for (int t = 0; t < TN; ++t) {
+    wreg[t] = *reinterpret_cast<const u32x4*>(wc[t]);
+    sreg[t] = *reinterpret_cast<const uint16_t*>(wsc[t]);
+  }
+#pragma unroll
+  for (int j = 0; j < A_PER_THREAD; ++j) {
+    int i = tid + 256 * j;
+    lds_a[0][lds_slot(i >> 3, i & 7)] = areg[j];
+  }
+
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    __syncthreads();
+    // prefetch the next K step
+    u32x4 wnext[TN];
+    uint32_t snext[TN];
+    const bool more = kt + 1 < KT;
+    if (more) {
+      const int koff = (kt + 1) * BK;
+#pragma unroll
+      for (int j = 0; j < A_PER_THREAD; ++j) areg[j] = a_rows[j][koff / 8];
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        wnext[t] = *reinterpret_cast<const u32x4*>(wc[t] + koff / 2);
+        snext[t] = *reinterpret_cast<const uint16_t*>(wsc[t] + koff / 16);
+      }
+    }
+    // compute on the current K step: 4 sub-steps of 16
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      f16x8 bfrag[TN];
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        uint32_t sb = (s < 2) ? (sreg[t] & 0xFFu) : (sreg[t] >> 8);
+        bfrag[t] = unpack8_f16(wreg[t][s], e4m3_to_f16x2(sb));
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        int r = wm * (BM / 2) + 32 * i + l32;
+        u32x4 av = lds_a[buf][lds_slot(r, 4 * g + s)];
+        f16x8 afrag = __builtin_bit_cast(f16x8, av);
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+          acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afrag, bfrag[t], acc[i][t], 0, 0, 0);
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int j = 0; j < A_PER_THREAD; ++j) {
+        int i = tid + 256 * j;
+        lds_a[buf ^ 1][lds_slot(i >> 3, i & 7)] = areg[j];
+      }
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        wreg[t] = wnext[t];
+        sreg[t] = snext[t];
+      }
+    }
+  }
+
+  // ---- epilogue: acc[i][t][r] = C[row = 8 (r/4) + 4 g + r%4][col = l32]
+  const float alpha = (*sga_ptr) * (*sgw_ptr);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+      const int n = n0 + wn * (BN / 2) + 32 * t + l32;
+      if (n >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * (BM / 2) + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (m >= M) continue;
+        float v = acc[i][t][r] * alpha;
+        if (bf16_out)
+          reinterpret_cast<uint16_t*>(y)[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_bits(v);
+        else
+          reinterpret_cast<float*>(y)[(int64_t)m * N + n] = v;
+      }
+    }
+  }
+}
+
+hipError_t launch_gemm_w4a4(const uint16_t* a_hat, const float* sga, const uint8_t* codes, const uint8_t* scales,
+                            const float* sgw, int64_t M, int64_t N, int64_t K, void* y, bool bf16_out,
+                            hipStream_t stream) {
+  int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
+  if (big >= 256) {
+    hipLaunchKernelGGL((gemm_w4a4_kernel<256, 256>), dim3((unsigned)big), dim3(256), 0, stream, a_hat, sga, codes,
+                       scales, sgw, (int)M, (int)N, (int)K, y, bf16_out ? 1 : 0);
+  } else {
+    int64_t small = ((M + 127) / 128) * ((N + 127) / 128);
+    hipLaunchKernelGGL((gemm_w4a4_kernel<128, 128>), dim3((unsigned)small), dim3(256), 0, stream, a_hat, sga, codes,
+                       scales, sgw, (int)M, (int)N, (int)K, y, bf16_out ? 1 : 0);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

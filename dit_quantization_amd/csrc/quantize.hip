@@ -1,0 +1,139 @@
+// NVFP4 quantizer kernels for gfx950: tensor amax -> s_g, and the absmax
+// block quantizer.
+//
+// "Tu pipeline NVFP4: meter 62 GB de modelo en 24 GB de laptop", section 2:
+// absmax places the block's largest magnitude on the top grid value
+// (s = max|W_k| / 6), each element is the nearest grid value of W/(s_b s_g),
+// and a per-tensor fp32 scale covers the tensor's range so the 8-bit block
+// scale only needs the block's range relative to it.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace nvfp4 {
+
+// ---------------------------------------------------------------- amax
+
+// Each workgroup reduces a grid-strided share of the tensor (16-byte loads)
+// to one partial max |x|.
+template <bool kBF16>
+__global__ __launch_bounds__(256) void amax_partial_kernel(const void* __restrict__ x, int64_t n_vec,
+                                                           float* __restrict__ partials) {
+  float m = 0.0f;
+  const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+  int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_vec; i += stride) {
+    u32x4 v = __builtin_nontemporal_load(&xv[i]);
+    if constexpr (kBF16) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        m = fmaxf(m, fabsf(bf16_bits_to_f32(v[j] & 0xFFFFu)));
+        m = fmaxf(m, fabsf(bf16_bits_to_f32(v[j] >> 16)));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m = fmaxf(m, fabsf(__uint_as_float(v[j])));
+    }
+  }
+  __shared__ float red[4];
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) partials[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__global__ __launch_bounds__(256) void amax_finalize_kernel(const float* __restrict__ partials, int np,
+                                                            float* __restrict__ sg_out) {
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < np; i += blockDim.x) m = fmaxf(m, partials[i]);
+  __shared__ float red[4];
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) *sg_out = global_scale_from_amax(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+}
+
+int amax_partial_count(int64_t n_elems, bool bf16) {
+  int64_t n_vec = n_elems / (bf16 ? 8 : 4);
+  int64_t wg = (n_vec + 256 * 8 - 1) / (256 * 8);  // ~8 vectors per thread
+  if (wg < 1) wg = 1;
+  if (wg > kMaxAmaxPartials) wg = kMaxAmaxPartials;
+  return (int)wg;
+}
+
+hipError_t launch_global_scale(const void* x, bool bf16, int64_t n_elems, float* partials, float* sg_out,
+                               hipStream_t stream) {
+  int np = amax_partial_count(n_elems, bf16);
+  int64_t n_vec = n_elems / (bf16 ? 8 : 4);
+  if (bf16)
+    hipLaunchKernelGGL(amax_partial_kernel<true>, dim3(np), dim3(256), 0, stream, x, n_vec, partials);
+  else
+    hipLaunchKernelGGL(amax_partial_kernel<false>, dim3(np), dim3(256), 0, stream, x, n_vec, partials);
+  hipLaunchKernelGGL(amax_finalize_kernel, dim3(1), dim3(256), 0, stream, partials, np, sg_out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- absmax quantizer
+
+// Load the 8 consecutive elements [8h, 8h+8) as fp32.
+template <bool kBF16>
+__device__ __forceinline__ void load8(const void* __restrict__ x, int64_t h, float w[8]) {
+  if constexpr (kBF16) {
+    u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x) + h);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w[2 * j] = bf16_bits_to_f32(v[j] & 0xFFFFu);
+      w[2 * j + 1] = bf16_bits_to_f32(v[j] >> 16);
+    }
+  } else {
+    const u32x4* p = reinterpret_cast<const u32x4*>(x) + 2 * h;
+    u32x4 a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w[j] = __uint_as_float(a[j]);
+      w[4 + j] = __uint_as_float(b[j]);
+    }
+  }
+}
+
+// One lane per half block (8 elements); lanes 2b and 2b+1 share block b.
+// x: flat [n] elements (rows*cols, cols % 16 == 0 so blocks never straddle
+// rows); codes: 4 bytes per lane; scales: one byte per block.
+template <bool kBF16>
+__global__ __launch_bounds__(256) void quantize_absmax_kernel(const void* __restrict__ x, int64_t n_half,
+                                                              const float* __restrict__ sg_ptr,
+                                                              uint32_t* __restrict__ codes,
+                                                              uint8_t* __restrict__ scales) {
+  const float sg = *sg_ptr;
+  const float inv_sg = 1.0f / sg;
+  const double six_sg = 6.0 * (double)sg;
+  int64_t stride = (int64_t)gridDim.x * blockDim.x;  // even
+  for (int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; h < n_half; h += stride) {
+    float w[8];
+    load8<kBF16>(x, h, w);
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(w[j]));
+    m = fmaxf(m, __shfl_xor(m, 1));
+    uint32_t sc = e4m3_code_rne((double)m / six_sg);
+    float sb = e4m3_to_f32(sc);
+    __builtin_nontemporal_store(encode8(w, sb, sg, inv_sg), &codes[h]);
+    if ((h & 1) == 0) scales[h >> 1] = (uint8_t)sc;
+  }
+}
+
+hipError_t launch_quantize_absmax(const void* x, bool bf16, int64_t n_elems, const float* sg, uint8_t* codes,
+                                  uint8_t* scales, hipStream_t stream) {
+  int64_t n_half = n_elems / 8;
+  if (n_half == 0) return hipSuccess;
+  int64_t wg = (n_half + 255) / 256;
+  if (wg > 8192) wg = 8192;
+  if (bf16)
+    hipLaunchKernelGGL(quantize_absmax_kernel<true>, dim3((unsigned)wg), dim3(256), 0, stream, x, n_half, sg,
+                       reinterpret_cast<uint32_t*>(codes), scales);
+  else
+    hipLaunchKernelGGL(quantize_absmax_kernel<false>, dim3((unsigned)wg), dim3(256), 0, stream, x, n_half, sg,
+                       reinterpret_cast<uint32_t*>(codes), scales);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,206 @@
+"""Python binding of libnvfp4.so (include/nvfp4.h): argument marshalling only.
+
+Every entry point takes torch tensors that live on the current HIP device and
+passes raw device pointers plus torch's current stream to the C ABI; all
+arithmetic runs in the library's gfx950 kernels.  A missing library raises at
+first use -- there is no fallback path.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_LAUNCH, ERR_FLAGS = range(9)
+F32, BF16 = 0, 1
+GLOBAL_COMPUTE, GLOBAL_GIVEN = 0, 1
+OP_QUANTIZE, OP_GEMM_W4A4, OP_GEMV_W4A16 = 0, 1, 2
+
+# name -> (restype, argtypes); mirrors include/nvfp4.h
+_P, _I, _I64, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+SIGNATURES = {
+    "nvfp4_quantize_absmax": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _I, _P, _SZ, _P]),
+    "nvfp4_quantize_mse": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _I, _P, _SZ, _P]),
+    "nvfp4_dequant": (_I, [_P, _P, _P, _I64, _I64, _P, _I, _P]),
+    "nvfp4_gemv_w4a16": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _SZ, _P]),
+    "nvfp4_gemm_w4a4": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _SZ, _P]),
+    "nvfp4_workspace_bytes": (_SZ, [_I, _I64, _I64]),
+    "nvfp4_status_string": (ctypes.c_char_p, [_I]),
+    "nvfp4_version": (_I, []),
+}
+
+_lib = None
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+
+
+def lib():
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m dit_quantization_amd.build` "
+                               "(hipcc, gfx950); there is no fallback implementation")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(status):
+    return lib().nvfp4_status_string(int(status)).decode()
+
+
+def workspace_bytes(op, a, b):
+    return int(lib().nvfp4_workspace_bytes(int(op), int(a), int(b)))
+
+
+def _check(fn, status):
+    if status != OK:
+        if status in (ERR_SHAPE, ERR_DTYPE, ERR_FLAGS, ERR_ALIGN, ERR_NULL):
+            raise ValueError(f"{fn}: {status_string(status)} (status {status})")
+        raise NVFP4Error(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(dt):
+    if dt == torch.float32:
+        return F32
+    if dt == torch.bfloat16:
+        return BF16
+    raise ValueError(f"unsupported dtype {dt}; expected float32 or bfloat16")
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous and on the GPU")
+
+
+def _alloc_ws(nbytes, device):
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _quantize(fn_name, x, global_scale=None, workspace=None, out=None):
+    _need_cuda(x)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, cols]")
+    rows, cols = x.shape
+    if cols % 16:
+        raise ValueError(f"cols={cols} is not a multiple of the 16-element block")
+    dev = x.device
+    if out is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
+        sg = torch.empty(1, dtype=torch.float32, device=dev)
+    else:
+        codes, scales, sg = out
+    flags = GLOBAL_COMPUTE
+    if global_scale is not None:
+        flags = GLOBAL_GIVEN
+        sg.copy_(torch.as_tensor(global_scale, dtype=torch.float32).reshape(1))
+        ws = None
+    else:
+        ws = workspace if workspace is not None else _alloc_ws(workspace_bytes(OP_QUANTIZE, rows, cols), dev)
+    st = getattr(lib(), fn_name)(_ptr(x), _dtype_code(x.dtype), rows, cols, _ptr(codes), _ptr(scales), _ptr(sg),
+                                 flags, _ptr(ws), 0 if ws is None else ws.numel(), _stream())
+    _check(fn_name, st)
+    return codes, scales, sg
+
+
+def quantize_absmax(x, global_scale=None, workspace=None, out=None):
+    """NVFP4 absmax quantization of a [rows, cols] fp32/bf16 GPU tensor.
+
+    Returns (codes uint8 [rows, cols/2], scales uint8 [rows, cols/16],
+    global scale fp32 [1]).  global_scale=None computes s_g on the device."""
+    return _quantize("nvfp4_quantize_absmax", x, global_scale, workspace, out)
+
+
+def quantize_mse(x, global_scale=None, workspace=None, out=None):
+    """NVFP4 quantization with MSE-searched block scales (same layout)."""
+    return _quantize("nvfp4_quantize_mse", x, global_scale, workspace, out)
+
+
+def dequant(codes, scales, global_scale, out_dtype=torch.float32, out=None):
+    _need_cuda(codes, scales, global_scale)
+    rows, half = codes.shape
+    cols = half * 2
+    if scales.shape != (rows, cols // 16):
+        raise ValueError(f"scales shape {tuple(scales.shape)} does not match codes {tuple(codes.shape)}")
+    if out is None:
+        out = torch.empty((rows, cols), dtype=out_dtype, device=codes.device)
+    st = lib().nvfp4_dequant(_ptr(codes), _ptr(scales), _ptr(global_scale), rows, cols, _ptr(out),
+                             _dtype_code(out.dtype), _stream())
+    _check("nvfp4_dequant", st)
+    return out
+
+
+def _check_weight(codes, scales, K):
+    N = codes.shape[0]
+    if codes.dtype != torch.uint8 or scales.dtype != torch.uint8:
+        raise ValueError("packed weights must be uint8 codes [N, K/2] and uint8 E4M3 scales [N, K/16]")
+    if tuple(codes.shape) != (N, K // 2) or tuple(scales.shape) != (N, K // 16):
+        raise ValueError(f"packed weight shapes {tuple(codes.shape)}, {tuple(scales.shape)} do not match "
+                         f"K={K}: expected [N, {K // 2}] and [N, {K // 16}]")
+    return N
+
+
+def gemv_w4a16(x, w_codes, w_scales, w_global, out_dtype=torch.bfloat16, workspace=None, out=None):
+    """y = x W^T for bf16 x [M, K] (M <= 16) and NVFP4 weights [N, K]."""
+    _need_cuda(x, w_codes, w_scales, w_global)
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("x must be a 2-D bfloat16 tensor")
+    M, K = x.shape
+    N = _check_weight(w_codes, w_scales, K)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    ws = workspace if workspace is not None else _alloc_ws(workspace_bytes(OP_GEMV_W4A16, M, N), x.device)
+    st = lib().nvfp4_gemv_w4a16(_ptr(x), _ptr(w_codes), _ptr(w_scales), _ptr(w_global), M, N, K, _ptr(out),
+                                _dtype_code(out.dtype), _ptr(ws), 0 if ws is None else ws.numel(), _stream())
+    _check("nvfp4_gemv_w4a16", st)
+    return out
+
+
+def gemm_w4a4(a, w_codes, w_scales, w_global, a_global=None, out_dtype=torch.bfloat16, workspace=None,
+              out=None):
+    """y = quant(a) W^T with per-call NVFP4 quantization of bf16 a [M, K].
+
+    a_global=None computes the activation's tensor scale on the device.
+    The workspace (returned contents documented in include/nvfp4.h) may be
+    passed in to inspect the quantized activation."""
+    _need_cuda(a, w_codes, w_scales, w_global, a_global)
+    if a.dtype != torch.bfloat16 or a.dim() != 2:
+        raise ValueError("a must be a 2-D bfloat16 tensor")
+    M, K = a.shape
+    N = _check_weight(w_codes, w_scales, K)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    ws = workspace if workspace is not None else _alloc_ws(workspace_bytes(OP_GEMM_W4A4, M, K), a.device)
+    st = lib().nvfp4_gemm_w4a4(_ptr(a), _ptr(a_global), _ptr(w_codes), _ptr(w_scales), _ptr(w_global), M, N, K,
+                               _ptr(out), _dtype_code(out.dtype), _ptr(ws), 0 if ws is None else ws.numel(),
+                               _stream())
+    _check("nvfp4_gemm_w4a4", st)
+    return out
+
+
+def gemm_workspace_layout(M, K):
+    """Byte offsets inside the W4A4 workspace: (s_gA, quantized activation fp16 [M, K])."""
+    return 0, 256

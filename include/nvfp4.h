@@ -71,7 +71,7 @@ typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1 } nvfp4_dtype;
 enum { NVFP4_GLOBAL_COMPUTE = 0, NVFP4_GLOBAL_GIVEN = 1 };
 
 /* operation ids for nvfp4_workspace_bytes */
-enum { NVFP4_OP_QUANTIZE = 0, NVFP4_OP_GEMM_W4A4 = 1 };
+enum { NVFP4_OP_QUANTIZE = 0, NVFP4_OP_GEMM_W4A4 = 1, NVFP4_OP_GEMV_W4A16 = 2 };
 
 /*
  * nvfp4_quantize_absmax -- NVFP4 encoding with absmax block scales.
@@ -127,12 +127,15 @@ int nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const float* glob
  *   y[m, n] = s_gW * sum_k x[m, k] * q[n, k] * s_b[n, k/16]
  *   x        [M, K] bf16;  w_codes [N, K/2];  w_scales [N, K/16];
  *   w_global 1 device fp32; y [M, N] of y_dtype (NVFP4_BF16 or NVFP4_F32)
- *   1 <= M <= 16 (the decode batch); fp32 accumulation, fp32 epilogue,
- *   round-to-nearest-even bf16 output.
+ *   workspace >= nvfp4_workspace_bytes(NVFP4_OP_GEMV_W4A16, M, N) bytes,
+ *            16-byte aligned: fp32 partial sums when the K range is split
+ *            across workgroups (contents on return unspecified)
+ *   0 <= M <= 16 (the decode batch; M = 0 or N = 0 is a no-op); fp32
+ *   accumulation, fp32 epilogue (x s_gW), round-to-nearest-even bf16 output.
  */
 int nvfp4_gemv_w4a16(const void* x, const uint8_t* w_codes, const uint8_t* w_scales,
                      const float* w_global, int64_t M, int64_t N, int64_t K,
-                     void* y, int y_dtype, void* stream);
+                     void* y, int y_dtype, void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * nvfp4_gemm_w4a4 -- y = A^ W^^T with the activation quantized to NVFP4 on
@@ -144,6 +147,8 @@ int nvfp4_gemv_w4a16(const void* x, const uint8_t* w_codes, const uint8_t* w_sca
  *            otherwise a device fp32 used as s_gA (a static activation scale)
  *   w_codes [N, K/2], w_scales [N, K/16], w_global: the NVFP4 weight
  *   y        [M, N] of y_dtype (NVFP4_BF16 or NVFP4_F32)
+ *   K % 64 == 0 (one K step of the kernel; all configured shapes qualify),
+ *   otherwise NVFP4_ERR_UNSUPPORTED.
  *   workspace >= nvfp4_workspace_bytes(NVFP4_OP_GEMM_W4A4, M, K) bytes,
  *            256-byte aligned.  On return it holds, at fixed offsets:
  *              [0, 4)       s_gA (fp32)
@@ -159,8 +164,9 @@ int nvfp4_gemm_w4a4(const void* a, const float* a_global, const uint8_t* w_codes
                     int64_t M, int64_t N, int64_t K, void* y, int y_dtype,
                     void* workspace, size_t ws_bytes, void* stream);
 
-/* Workspace size in bytes for an operation (NVFP4_OP_QUANTIZE with
- * (rows, cols), NVFP4_OP_GEMM_W4A4 with (M, K)); 0 for an unknown op. */
+/* Workspace size in bytes for an operation: NVFP4_OP_QUANTIZE with
+ * (rows, cols), NVFP4_OP_GEMM_W4A4 with (M, K), NVFP4_OP_GEMV_W4A16 with
+ * (M, N); 0 for an unknown op or negative sizes. */
 size_t nvfp4_workspace_bytes(int op, int64_t rows_or_m, int64_t cols_or_k);
 
 /* Static, NUL-terminated description of a status code. */

@@ -1,0 +1,114 @@
+"""C-ABI library checks that need no GPU: it loads, exports every symbol the
+header declares, and rejects bad arguments before touching the HIP runtime."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from dit_quantization_amd import nvfp4 as nv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+A16 = 0x10000          # fake, aligned, non-null addresses: validation never dereferences
+A4 = 0x10004
+BIG = 1 << 40
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = nv.lib()
+    names = header_functions()
+    assert len(names) == 8, names
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in nv.SIGNATURES, n
+
+
+def test_status_strings_and_version():
+    assert nv.lib().nvfp4_version() == 10000
+    for s in range(9):
+        assert nv.status_string(s) and nv.status_string(s) != "unknown status"
+    assert nv.status_string(99) == "unknown status"
+
+
+def test_workspace_sizes():
+    assert nv.workspace_bytes(nv.OP_QUANTIZE, 4096, 4096) >= 4 * 1 and nv.workspace_bytes(nv.OP_QUANTIZE, 4096, 4096) % 256 == 0
+    g = nv.workspace_bytes(nv.OP_GEMM_W4A4, 4096, 4096)
+    assert g >= 256 + 2 * 4096 * 4096
+    assert nv.workspace_bytes(nv.OP_GEMV_W4A16, 16, 4096) >= 8 * 16 * 4096 * 4
+    assert nv.workspace_bytes(99, 1, 1) == 0
+    assert nv.workspace_bytes(nv.OP_QUANTIZE, -1, 16) == 0
+
+
+def q(fn, x=A16, dt=nv.F32, rows=4, cols=64, codes=A16, scales=A16, gs=A4, flags=nv.GLOBAL_GIVEN, ws=None, wsb=0):
+    return getattr(nv.lib(), fn)(x, dt, rows, cols, codes, scales, gs, flags, ws, wsb, None)
+
+
+@pytest.mark.parametrize("fn", ["nvfp4_quantize_absmax", "nvfp4_quantize_mse"])
+def test_quantize_validation(fn):
+    assert q(fn, x=None) == nv.ERR_NULL
+    assert q(fn, codes=None) == nv.ERR_NULL
+    assert q(fn, gs=None) == nv.ERR_NULL
+    assert q(fn, dt=7) == nv.ERR_DTYPE
+    assert q(fn, flags=4) == nv.ERR_FLAGS
+    assert q(fn, rows=-1) == nv.ERR_SHAPE
+    assert q(fn, cols=24) == nv.ERR_SHAPE          # not a multiple of the 16-element block
+    assert q(fn, cols=48) == nv.ERR_UNSUPPORTED    # a valid block count, off the K % 32 fast path
+    assert q(fn, rows=BIG, cols=BIG) == nv.ERR_SHAPE
+    assert q(fn, x=A16 + 4) == nv.ERR_ALIGN
+    assert q(fn, codes=A16 + 2) == nv.ERR_ALIGN
+    assert q(fn, flags=nv.GLOBAL_COMPUTE, ws=None) == nv.ERR_WORKSPACE
+    assert q(fn, flags=nv.GLOBAL_COMPUTE, ws=A16, wsb=4) == nv.ERR_WORKSPACE
+
+
+def test_dequant_validation():
+    L = nv.lib()
+    assert L.nvfp4_dequant(None, A16, A4, 4, 64, A16, nv.F32, None) == nv.ERR_NULL
+    assert L.nvfp4_dequant(A16, A16, A4, 4, 64, A16, 3, None) == nv.ERR_DTYPE
+    assert L.nvfp4_dequant(A16, A16, A4, 4, 40, A16, nv.F32, None) == nv.ERR_SHAPE
+    assert L.nvfp4_dequant(A16, A16, A4, 4, 48, A16, nv.F32, None) == nv.ERR_UNSUPPORTED
+    assert L.nvfp4_dequant(A16, A16, A4, 4, 64, A16 + 8, nv.F32, None) == nv.ERR_ALIGN
+
+
+def test_gemv_validation():
+    L = nv.lib()
+    f = L.nvfp4_gemv_w4a16
+    assert f(None, A16, A16, A4, 1, 64, 64, A16, nv.BF16, None, 0, None) == nv.ERR_NULL
+    assert f(A16, A16, A16, A4, 1, 64, 64, A16, 5, None, 0, None) == nv.ERR_DTYPE
+    assert f(A16, A16, A16, A4, 1, 64, 40, A16, nv.BF16, None, 0, None) == nv.ERR_SHAPE
+    assert f(A16, A16, A16, A4, 17, 64, 64, A16, nv.BF16, None, 0, None) == nv.ERR_UNSUPPORTED
+    assert f(A16, A16, A16, A4, 1, 64, 48, A16, nv.BF16, None, 0, None) == nv.ERR_UNSUPPORTED
+    assert f(A16 + 2, A16, A16, A4, 1, 64, 64, A16, nv.BF16, None, 0, None) == nv.ERR_ALIGN
+    assert f(A16, A16, A16, A4, 0, 64, 64, A16, nv.BF16, None, 0, None) == nv.OK      # empty: no launch
+    # a split-K plan needs the workspace
+    assert f(A16, A16, A16, A4, 16, 4096, 14336, A16, nv.BF16, None, 0, None) == nv.ERR_WORKSPACE
+
+
+def test_gemm_validation():
+    L = nv.lib()
+    f = L.nvfp4_gemm_w4a4
+    W = 1 << 30
+    assert f(None, None, A16, A16, A4, 64, 64, 64, A16, nv.BF16, A16, W, None) == nv.ERR_NULL
+    assert f(A16, None, A16, A16, A4, 64, 64, 64, A16, nv.BF16, None, W, None) == nv.ERR_NULL
+    assert f(A16, None, A16, A16, A4, 64, 64, 64, A16, 9, A16, W, None) == nv.ERR_DTYPE
+    assert f(A16, None, A16, A16, A4, 64, 64, 40, A16, nv.BF16, A16, W, None) == nv.ERR_SHAPE
+    assert f(A16, None, A16, A16, A4, 64, 64, 96, A16, nv.BF16, A16, W, None) == nv.ERR_UNSUPPORTED
+    assert f(A16, None, A16, A16, A4, 64, 64, 64, A16, nv.BF16, A16 + 16, W, None) == nv.ERR_ALIGN
+    assert f(A16, None, A16, A16, A4, 64, 64, 64, A16, nv.BF16, A16, 16, None) == nv.ERR_WORKSPACE
+    assert f(A16, None, A16, A16, A4, 0, 64, 64, A16, nv.BF16, A16, W, None) == nv.OK
+
+
+def test_python_layer_rejects_mismatched_packed_shapes():
+    import torch
+    codes = torch.zeros((8, 32), dtype=torch.uint8)
+    scales = torch.zeros((8, 4), dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        nv._check_weight(codes, scales, 128)          # codes halved twice, as a BF16-read-as-FP4 mistake
+    assert nv._check_weight(codes, scales, 64) == 8

@@ -1,0 +1,155 @@
+"""GPU parity of the W4A16 GEMV and the W4A4 GEMM against the fp64 oracle:
+fp32 outputs within tau = 1e-5 * sum |a||w| of y*, bf16 outputs inside
+[bf16(y* - tau), bf16(y* + tau)]; the activation quantization inside the
+W4A4 call is checked bit-exactly through its documented workspace."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dit_quantization_amd import inputs
+from dit_quantization_amd import nvfp4 as nv
+from tests.gpu_helpers import DEV, assert_bracket_bf16, assert_within_tau, dev_bf16, dev_f32, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _quant_weight(w, method=oracle.ABSMAX):
+    fn = nv.quantize_absmax if method == oracle.ABSMAX else nv.quantize_mse
+    c, s, g = fn(dev_f32(w))
+    return c, s, g
+
+
+def test_tiny_config_gemv():
+    w, xb = inputs.tiny()
+    c, s, g = _quant_weight(w)
+    oc, os_, og = oracle.quantize(w)
+    assert np.array_equal(host(c), oc) and np.array_equal(host(s), os_)
+    x = inputs.bf16_bits_to_f32(xb)
+    ystar, tau = oracle.dot_w4a16(x, oc, os_, og)
+    yb = host(nv.gemv_w4a16(dev_bf16(xb), c, s, g))
+    assert_bracket_bf16(yb.reshape(-1), ystar, tau, "tiny bf16")
+    y32 = host(nv.gemv_w4a16(dev_bf16(xb), c, s, g, out_dtype=torch.float32))
+    assert_within_tau(y32.reshape(-1), ystar, tau, "tiny fp32")
+
+
+@pytest.mark.parametrize("shape", [(64, 32), (100, 160), (1000, 1056), (33, 4096)])
+@pytest.mark.parametrize("M", [1, 3, 16])
+def test_gemv_ragged(shape, M):
+    N, K = shape
+    print(f"[case] gemv N={N} K={K} M={M}", flush=True)
+    w = inputs.student_t_f32((N, K), N + K)
+    xb = inputs.gemv_x(K, M)
+    c, s, g = _quant_weight(w, oracle.MSE)
+    oc, os_, og = host(c), host(s), float(host(g)[0])
+    ystar, tau = oracle.dot_w4a16(inputs.bf16_bits_to_f32(xb), oc, os_, og)
+    y32 = host(nv.gemv_w4a16(dev_bf16(xb), c, s, g, out_dtype=torch.float32))
+    assert_within_tau(y32.reshape(-1), ystar, tau, "fp32")
+    yb = host(nv.gemv_w4a16(dev_bf16(xb), c, s, g))
+    assert_bracket_bf16(yb.reshape(-1), ystar, tau, "bf16")
+
+
+@pytest.mark.parametrize("which", [0, 1])
+def test_gemv_decode_full_size(which):
+    w = inputs.gemv_weights()[which]
+    N, K = w.shape
+    print(f"[case] gemv full N={N} K={K}", flush=True)
+    c, s, g = _quant_weight(w)
+    oc, os_, og = oracle.quantize(w)
+    assert float(host(g)[0]) == og
+    assert np.array_equal(host(s), os_) and np.array_equal(host(c), oc)   # full-size absmax parity
+    xb = inputs.gemv_x(K, 16)
+    x = inputs.bf16_bits_to_f32(xb)
+    ystar, tau = oracle.dot_w4a16(x, oc, os_, og)
+    ystar = ystar.reshape(16, N)
+    tau = tau.reshape(16, N)
+    for M in (1, 4, 16):
+        xd = dev_bf16(xb[:M])
+        yb = host(nv.gemv_w4a16(xd, c, s, g))
+        assert_bracket_bf16(yb.reshape(-1), ystar[:M].reshape(-1), tau[:M].reshape(-1), f"M={M}")
+        y32 = host(nv.gemv_w4a16(xd, c, s, g, out_dtype=torch.float32))
+        assert_within_tau(y32.reshape(-1), ystar[:M].reshape(-1), tau[:M].reshape(-1), f"M={M} fp32")
+
+
+def _check_gemm(ab, w_c, w_s, w_g, pairs=None, a_global=None, what=""):
+    M, K = ab.shape
+    N = w_c.shape[0]
+    print(f"[case] gemm {what} M={M} N={N} K={K}", flush=True)
+    ws = torch.empty(nv.workspace_bytes(nv.OP_GEMM_W4A4, M, K), dtype=torch.uint8, device=DEV)
+    a_dev = dev_bf16(ab)
+    ag = None if a_global is None else torch.tensor([a_global], dtype=torch.float32, device=DEV)
+    y32 = nv.gemm_w4a4(a_dev, w_c, w_s, w_g, a_global=ag, out_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    # activation quantization: s_gA and q_a * s_a (fp16) in the workspace
+    a32 = inputs.bf16_bits_to_f32(ab)
+    ac, as_, asg = oracle.quantize(a32, oracle.ABSMAX, sg=a_global)
+    wsh = host(ws)
+    assert wsh[:4].view(np.float32)[0] == np.float32(asg)
+    ahat = wsh[256:256 + 2 * M * K].view(np.float16).reshape(M, K).astype(np.float32)
+    want = oracle.dequant(ac, as_, 1.0, M, K)
+    assert np.array_equal(ahat, want), np.argwhere(ahat != want)[:5]
+    # products
+    oc, os_, og = host(w_c), host(w_s), float(host(w_g)[0])
+    if pairs is None:
+        ystar, tau = oracle.dot_w4a4(ac, as_, asg, oc, os_, og, K)
+        sel = slice(None)
+    else:
+        ystar, tau = oracle.dot_w4a4(ac, as_, asg, oc, os_, og, K, pairs=pairs, M=M, N=N)
+        sel = (pairs[0], pairs[1])
+    assert_within_tau(host(y32)[sel].reshape(-1), ystar, tau, what + " fp32")
+    yb = nv.gemm_w4a4(a_dev, w_c, w_s, w_g, a_global=ag, workspace=ws)
+    assert_bracket_bf16(host(yb)[sel].reshape(-1), ystar, tau, what + " bf16")
+
+
+@pytest.mark.parametrize("mnk", [(1, 64, 64), (70, 130, 192), (300, 520, 512), (257, 300, 4096)])
+def test_gemm_ragged_full_compare(mnk):
+    M, N, K = mnk
+    a = inputs.normal_f32((M, K), M + 1)
+    a, _ = inputs.with_outlier_columns(a, max(1, K // 100), 3)
+    ab = inputs.to_bf16_bits(a)
+    w = inputs.student_t_f32((N, K), N + 2)
+    c, s, g = _quant_weight(w, oracle.MSE)
+    _check_gemm(ab, c, s, g, what=str(mnk))
+
+
+def test_gemm_static_activation_scale():
+    a = inputs.normal_f32((96, 256), 11)
+    ab = inputs.to_bf16_bits(a)
+    c, s, g = _quant_weight(inputs.student_t_f32((128, 256), 12))
+    _check_gemm(ab, c, s, g, a_global=0.01, what="static s_gA")
+
+
+def _sample_pairs(M, N, n, seed):
+    g = inputs.rng(seed)
+    pm = np.concatenate([[0, M - 1, 0, M - 1], g.integers(0, M, n)])
+    pn = np.concatenate([[0, 0, N - 1, N - 1], g.integers(0, N, n)])
+    return pm.astype(np.int64), pn.astype(np.int64)
+
+
+def test_gemm_prefill_full_size_sampled():
+    ab = inputs.prefill_activation()
+    (_, w), = list(inputs.layerset(["gate"]))
+    c, s, g = _quant_weight(w, oracle.MSE)
+    _check_gemm(ab, c, s, g, pairs=_sample_pairs(4096, 14336, 3000, 1), what="prefill")
+
+
+def test_gemm_dit_block_sampled():
+    a_img, a_txt, h_img, h_txt = inputs.dit_activations()
+    for stream, (a, h) in enumerate(((a_img, h_img), (a_txt, h_txt))):
+        for name, w in inputs.dit_weights(stream):
+            c, s, g = _quant_weight(w, oracle.MSE)
+            act = h if name == "mlp_down" else a
+            M, N = act.shape[0], w.shape[0]
+            _check_gemm(act, c, s, g, pairs=_sample_pairs(M, N, 600, stream * 10 + len(name)),
+                        what=f"dit stream{stream} {name}")
+
+
+def test_gemm_and_gemv_deterministic():
+    ab = inputs.to_bf16_bits(inputs.normal_f32((256, 512), 1))
+    c, s, g = _quant_weight(inputs.student_t_f32((384, 512), 2))
+    y1 = host(nv.gemm_w4a4(dev_bf16(ab), c, s, g))
+    y2 = host(nv.gemm_w4a4(dev_bf16(ab), c, s, g))
+    assert np.array_equal(y1, y2)
+    v1 = host(nv.gemv_w4a16(dev_bf16(ab[:16]), c, s, g))
+    v2 = host(nv.gemv_w4a16(dev_bf16(ab[:16]), c, s, g))
+    assert np.array_equal(v1, v2)
