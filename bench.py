@@ -1,0 +1,395 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 hot path on one MI355X.
+
+One step runs every stage of the path once over synthetic inputs resident in
+HBM:
+  quantize  the 8B-shaped layer set (q, k, v, o, gate, up, down; Student-t
+            x 0.02, fp32): absmax with a computed tensor scale (amax pass +
+            quantize pass), the absmax pass alone with that scale given,
+            and the MSE scale search with that scale given;
+  gemv      W4A16 decode: W [14336, 4096] and [4096, 14336], M = 1, 4, 16
+            (weights rotated over enough copies to defeat the 256 MB MALL);
+  gemm      W4A4 prefill: A [4096, 4096] bf16 with 1 % x20 outlier columns
+            against gate and up [14336, 4096] (gate quantizes A, up reuses it);
+            a Flux-like double-stream DiT block: image M = 4096 and text
+            M = 512 tokens, to_q/k/v 3072x3072 (k, v reuse q's activation),
+            MLP up 12288x3072 and down 3072x12288.
+Every stage is launched eagerly on torch's current stream (the stream the
+library launches on) between two HIP events; before each stage a short GPU
+spin kernel holds the queue so the host has enqueued the whole stage before
+it starts, and the events time only GPU work (no host launch gaps).  The printed JSON line reports
+value = mean over {quantize pass HBM %, GEMV HBM %, W4A4 GEMM MFMA %} of the
+fraction of MI355X peak, plus per-stage numbers, the roofline of the
+dominant kernel and the CPU oracle timed on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK = 8.0e12           # bytes/s
+MFMA16_PEAK = 2.5e15        # dense fp16/bf16 MFMA flop/s
+VALU_PEAK = 256 * 64 * 2.4e9  # non-packed fp32/fp64 lane-ops/s: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz
+GEMV_COPIES = 8             # 8 x 33 MB > 256 MB MALL
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--phases", default="quantize,gemv,gemm")
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def e4m3_table():
+    vals = [m / 8 * 2.0 ** -6 for m in range(8)]
+    for e in range(1, 16):
+        for m in range(8):
+            if e == 15 and m == 7:
+                continue
+            vals.append((1 + m / 8) * 2.0 ** (e - 7))
+    return np.array(vals)
+
+
+def mse_candidates(x, sg):
+    """Number of scale candidates the MSE search visits per block (host count,
+    used only to express the search's work against the ALU roofline)."""
+    e4 = e4m3_table()
+    amax = np.abs(x.reshape(-1, 16)).max(axis=1).astype(np.float64)
+    a = amax / (6.0 * sg)
+    lo = np.searchsorted(e4[1:], a / 2, side="left") + 1
+    hi = np.searchsorted(e4[1:], np.minimum(2 * a, 448.0), side="right")
+    return np.maximum(hi - lo + 1, 1).sum()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU split of this path is "
+              "described in DESIGN.md and not built", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from dit_quantization_amd import inputs
+    from dit_quantization_amd import nvfp4 as nv
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    phases = set(args.phases.split(","))
+    t0 = time.time()
+
+    def f32(x):
+        return torch.from_numpy(x).to(dev)
+
+    def bf16(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    stream = torch.cuda.current_stream()
+
+    stages = {}   # name -> (stage function, calls, algorithmic bytes, flops, alu ops per run)
+
+    def capture(name, fn, nbytes=0.0, flops=0.0, ops=0.0, calls=1):
+        log(f"[stage] {name}: first run")
+        fn()                                  # first run: loads code objects, checks the arguments
+        torch.cuda.synchronize()
+        stages[name] = (fn, calls, nbytes, flops, ops)
+
+    # ------------------------------------------------------------ quantize
+    layer_elems = 0
+    if "quantize" in phases:
+        log("[setup] layer set")
+        qbuf = []
+        mse_ops = 0.0
+        for name, w in inputs.layerset():
+            xd = f32(w)
+            rows, cols = w.shape
+            out_a = (torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
+                     torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev),
+                     torch.empty(1, dtype=torch.float32, device=dev))
+            out_m = (torch.empty_like(out_a[0]), torch.empty_like(out_a[1]), torch.empty_like(out_a[2]))
+            ws = torch.empty(nv.workspace_bytes(nv.OP_QUANTIZE, rows, cols), dtype=torch.uint8, device=dev)
+            nv.quantize_absmax(xd, workspace=ws, out=out_a)
+            torch.cuda.synchronize()
+            sg = float(out_a[2].item())
+            out_m[2].fill_(sg)
+            qbuf.append((xd, out_a, out_m, ws, sg, rows, cols))
+            layer_elems += rows * cols
+            mse_ops += mse_candidates(w, sg) * 16 * 6.0
+            del w
+        n = layer_elems
+
+        def q_dynamic():
+            for xd, out_a, out_m, ws, sg, rows, cols in qbuf:
+                nv.quantize_absmax(xd, workspace=ws, out=out_a)
+
+        def q_pass():
+            for xd, out_a, out_m, ws, sg, rows, cols in qbuf:
+                nv.lib().nvfp4_quantize_absmax(nv._ptr(xd), nv.F32, rows, cols, nv._ptr(out_a[0]),
+                                               nv._ptr(out_a[1]), nv._ptr(out_a[2]), nv.GLOBAL_GIVEN, None, 0,
+                                               nv._stream())
+
+        def q_mse():
+            for xd, out_a, out_m, ws, sg, rows, cols in qbuf:
+                nv.lib().nvfp4_quantize_mse(nv._ptr(xd), nv.F32, rows, cols, nv._ptr(out_m[0]), nv._ptr(out_m[1]),
+                                            nv._ptr(out_m[2]), nv.GLOBAL_GIVEN, None, 0, nv._stream())
+
+        capture("quantize_absmax_dynamic", q_dynamic, nbytes=n * (4 + 4 + 0.5625))
+        capture("quantize_absmax_pass", q_pass, nbytes=n * (4 + 0.5625))
+        capture("quantize_mse", q_mse, nbytes=n * (4 + 0.5625), ops=mse_ops)
+
+    # ------------------------------------------------------------ gemv
+    if "gemv" in phases:
+        log("[setup] gemv weights")
+        for wi, w in enumerate(inputs.gemv_weights()):
+            N, K = w.shape
+            c, s, g = nv.quantize_absmax(f32(w))
+            copies = [(c.clone(), s.clone()) for _ in range(GEMV_COPIES)]
+            del c, s
+            xb = bf16(inputs.gemv_x(K, 16))
+            for M in (1, 4, 16):
+                xm = xb[:M].contiguous()
+                ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(GEMV_COPIES)]
+                ws = torch.empty(max(nv.workspace_bytes(nv.OP_GEMV_W4A16, M, N), 256), dtype=torch.uint8, device=dev)
+
+                def run(copies=copies, xm=xm, ys=ys, ws=ws, g=g):
+                    for (cc, ss), y in zip(copies, ys):
+                        nv.gemv_w4a16(xm, cc, ss, g, workspace=ws, out=y)
+
+                nbytes = GEMV_COPIES * (N * K * 0.5625 + 2 * M * K + 2 * M * N)
+                capture(f"gemv_{N}x{K}_M{M}", run, nbytes=nbytes, flops=GEMV_COPIES * 2.0 * M * N * K,
+                        calls=GEMV_COPIES)
+            del w
+
+    # ------------------------------------------------------------ gemm
+    if "gemm" in phases:
+        log("[setup] prefill")
+        a = bf16(inputs.prefill_activation())
+        wts = {}
+        for name, w in inputs.layerset(["gate", "up"]):
+            wts[name] = nv.quantize_mse(f32(w))
+            del w
+        M, K = a.shape
+        N = wts["gate"][0].shape[0]
+        ws = torch.empty(nv.workspace_bytes(nv.OP_GEMM_W4A4, M, K), dtype=torch.uint8, device=dev)
+        y_gate = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        y_up = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+        def prefill_gate():
+            nv.gemm_w4a4(a, *wts["gate"], workspace=ws, out=y_gate)
+
+        def prefill_up():
+            nv.gemm_w4a4(a, *wts["up"], workspace=ws, out=y_up, reuse_act=True)
+
+        capture("gemm_prefill_gate_actquant", prefill_gate, flops=2.0 * M * N * K,
+                nbytes=M * K * (2 + 2 + 2 + 2) + N * K * 0.5625 + 2 * M * N)
+        capture("gemm_prefill_up_reuse", prefill_up, flops=2.0 * M * N * K,
+                nbytes=M * K * 2 + N * K * 0.5625 + 2 * M * N)
+
+        log("[setup] dit block")
+        a_img, a_txt, h_img, h_txt = inputs.dit_activations()
+        dit_calls = []
+        for stream_id, (aa, hh) in enumerate(((a_img, h_img), (a_txt, h_txt))):
+            ad, hd = bf16(aa), bf16(hh)
+            Ms = aa.shape[0]
+            w = {name: nv.quantize_mse(f32(x)) for name, x in inputs.dit_weights(stream_id)}
+            ws_a = torch.empty(nv.workspace_bytes(nv.OP_GEMM_W4A4, Ms, ad.shape[1]), dtype=torch.uint8, device=dev)
+            ws_h = torch.empty(nv.workspace_bytes(nv.OP_GEMM_W4A4, Ms, hd.shape[1]), dtype=torch.uint8, device=dev)
+            outs = {name: torch.empty((Ms, w[name][0].shape[0]), dtype=torch.bfloat16, device=dev) for name in w}
+            dit_calls.append((ad, hd, w, ws_a, ws_h, outs))
+        dit_flops = 0.0
+        for ad, hd, w, ws_a, ws_h, outs in dit_calls:
+            for name, (c, s, g) in w.items():
+                dit_flops += 2.0 * ad.shape[0] * c.shape[0] * c.shape[1] * 2
+
+        def dit_block():
+            for ad, hd, w, ws_a, ws_h, outs in dit_calls:
+                nv.gemm_w4a4(ad, *w["to_q"], workspace=ws_a, out=outs["to_q"])
+                nv.gemm_w4a4(ad, *w["to_k"], workspace=ws_a, out=outs["to_k"], reuse_act=True)
+                nv.gemm_w4a4(ad, *w["to_v"], workspace=ws_a, out=outs["to_v"], reuse_act=True)
+                nv.gemm_w4a4(ad, *w["mlp_up"], workspace=ws_a, out=outs["mlp_up"])   # the MLP input is quantized anew
+                nv.gemm_w4a4(hd, *w["mlp_down"], workspace=ws_h, out=outs["mlp_down"])
+
+        capture("gemm_dit_block", dit_block, flops=dit_flops)
+
+    torch.cuda.synchronize()
+    log(f"[setup] done in {time.time() - t0:.1f}s; stages: {list(stages)}")
+
+    # ------------------------------------------------------------ timing
+    names = list(stages)
+    ev = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for k in names}
+    acc = {k: 0.0 for k in names}
+    step_start, step_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    # GPU spin long enough for the host to enqueue any one stage behind it
+    spin = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    spin[0].record(stream)
+    torch.cuda._sleep(1 << 20)
+    spin[1].record(stream)
+    torch.cuda.synchronize()
+    cycles = int((1 << 20) * 2.0 / max(spin[0].elapsed_time(spin[1]), 1e-3))   # ~2 ms
+
+    def one_step(record):
+        for k in names:
+            torch.cuda._sleep(cycles)
+            if record:
+                ev[k][0].record(stream)
+            stages[k][0]()
+            if record:
+                ev[k][1].record(stream)
+
+    log("[timing] warmup")
+    for _ in range(args.warmup):
+        one_step(False)
+    torch.cuda.synchronize()
+    total_ms = 0.0
+    log("[timing] timed steps")
+    for _ in range(args.steps):
+        step_start.record(stream)
+        one_step(True)
+        step_end.record(stream)
+        torch.cuda.synchronize()
+        total_ms += step_start.elapsed_time(step_end)
+        for k in names:
+            acc[k] += ev[k][0].elapsed_time(ev[k][1])
+    ms_per_step = sum(acc.values()) / args.steps     # GPU work per step (spins excluded)
+    wall_ms_per_step = total_ms / args.steps
+    per = {}
+    for k in names:
+        g, calls, nbytes, flops, ops = stages[k]
+        t = acc[k] / args.steps / 1e3     # seconds per replay
+        per[k] = {"us": t * 1e6, "us_per_call": t * 1e6 / calls}
+        if nbytes:
+            per[k]["GB_s"] = nbytes / t / 1e9
+            per[k]["hbm_frac"] = nbytes / t / HBM_PEAK
+        if flops:
+            per[k]["TFLOP_s"] = flops / t / 1e12
+            per[k]["mfma_frac"] = flops / t / MFMA16_PEAK
+        if ops:
+            per[k]["Gops_s"] = ops / t / 1e9
+            per[k]["valu_frac"] = ops / t / VALU_PEAK
+        log(f"  {k:32s} {json.dumps(per[k])}")
+
+    comps = {}
+    if "quantize_absmax_pass" in per:
+        comps["quantize_hbm_frac"] = per["quantize_absmax_pass"]["hbm_frac"]
+    gv = [k for k in per if k.startswith("gemv_")]
+    if gv:
+        tb = sum(stages[k][2] for k in gv)
+        tt = sum(per[k]["us"] for k in gv) / 1e6
+        comps["gemv_hbm_frac"] = tb / tt / HBM_PEAK
+        comps["gemv_GB_s"] = tb / tt / 1e9
+    gm = [k for k in per if k.startswith("gemm_")]
+    if gm:
+        tf = sum(stages[k][3] for k in gm)
+        tt = sum(per[k]["us"] for k in gm) / 1e6
+        comps["gemm_mfma_frac"] = tf / tt / MFMA16_PEAK
+        comps["gemm_TFLOP_s"] = tf / tt / 1e12
+    fracs = [comps[k] for k in ("quantize_hbm_frac", "gemv_hbm_frac", "gemm_mfma_frac") if k in comps]
+    value = 100.0 * sum(fracs) / len(fracs) if fracs else 0.0
+
+    # dominant kernel: the stage with the largest share of the step time
+    dom = max(names, key=lambda k: per[k]["us"])
+    roofline = None
+    kernel_of = {
+        "quantize_mse": ("quantize_mse_kernel", "alu"),
+        "quantize_absmax_pass": ("quantize_absmax_kernel", "hbm"),
+        "gemm_prefill_up_reuse": ("gemm_w4a4_kernel<256,256>", "mfma"),
+    }
+    if dom.startswith("gemm_"):
+        dom = "gemm_prefill_up_reuse" if "gemm_prefill_up_reuse" in per else dom
+    if dom in kernel_of:
+        kname, bound = kernel_of[dom]
+        g, calls, nbytes, flops, ops = stages[dom]
+        t = per[dom]["us"] / 1e6
+        if bound == "mfma":
+            roofline = {"bound": "mfma", "kernel": kname, "achieved": flops / t / 1e12, "peak": 2500.0,
+                        "unit": "TFLOP/s", "frac": flops / t / MFMA16_PEAK, "traffic": None}
+        elif bound == "alu":
+            roofline = {"bound": "alu", "kernel": kname, "achieved": ops / t / 1e12, "peak": VALU_PEAK / 1e12,
+                        "unit": "Tops/s", "frac": ops / t / VALU_PEAK, "traffic": None}
+        else:
+            roofline = {"bound": "hbm", "kernel": kname, "achieved": nbytes / t / 1e9, "peak": 8000.0,
+                        "unit": "GB/s", "frac": nbytes / t / HBM_PEAK, "traffic": None}
+        roofline["launch_us"] = per[dom]["us_per_call"] if calls == 1 else per[dom]["us"]
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(comps)
+
+    line = {
+        "metric": "quantize GB/s + W4A16 GEMV GB/s + W4A4 GEMM TFLOP/s, each as % of MI355X peak",
+        "value": round(value, 3),
+        "unit": "% of MI355X peak (mean of quantize-pass HBM, GEMV HBM, W4A4 GEMM MFMA fractions)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "wall_ms_per_step_incl_queue_spins": round(wall_ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "nvfp4 (e2m1 codes, e4m3 scales) -> f16/bf16 mfma, f32 accumulate",
+        "data": "synthetic (seeded numpy PCG64; Student-t/Gaussian weights, outlier-channel activations)",
+        "config": {"workload": "nvfp4 hot path: 8B layer-set quantize (absmax + MSE), decode GEMV "
+                               "14336x4096 / 4096x14336 at M=1,4,16, W4A4 prefill 4096x4096x14336 (gate+up), "
+                               "Flux-like double-stream DiT block (img 4096 + txt 512 tokens, hidden 3072)",
+                   "layer_set_elements": layer_elems},
+        "components": {k: round(v, 5) for k, v in comps.items()},
+        "stages": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in per.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(gpu_comps):
+    """The CPU oracle (plain C, fp64, OpenMP over blocks/pairs) on a bounded
+    sample of the same workloads, expressed in the same unit."""
+    import oracle
+    from dit_quantization_amd import inputs
+    cores = len(os.sched_getaffinity(0))
+    res = {}
+    # quantize (absmax) on the layer set's q tensor (2^24 elements)
+    (_, w), = list(inputs.layerset(["q"]))
+    xs = w
+    t = time.perf_counter()
+    oracle.quantize(xs, oracle.ABSMAX, threads=cores)
+    dt = time.perf_counter() - t
+    qfrac = xs.size * (4 + 4 + 0.5625) / dt / HBM_PEAK
+    res["quantize_GB_s"] = xs.size * (4 + 4 + 0.5625) / dt / 1e9
+    # MSE on 2^20 elements
+    xm = w[:256]
+    t = time.perf_counter()
+    oracle.quantize(xm, oracle.MSE, threads=cores)
+    res["mse_GB_s"] = xm.size * (4 + 0.5625) / (time.perf_counter() - t) / 1e9
+    # GEMV: M = 1 against 4096 rows of the 14336 x 4096 weight
+    w1 = inputs.normal_f32((4096, 4096), 1, 0.02)
+    c, s, sg = oracle.quantize(w1, threads=cores)
+    x = inputs.bf16_bits_to_f32(inputs.gemv_x(4096, 1))
+    t = time.perf_counter()
+    oracle.dot_w4a16(x, c, s, sg, threads=cores)
+    dt = time.perf_counter() - t
+    gbytes = 4096 * 4096 * 0.5625 + 2 * 4096 + 2 * 4096
+    gfrac = gbytes / dt / HBM_PEAK
+    res["gemv_GB_s"] = gbytes / dt / 1e9
+    # W4A4: 128 x 1024 outputs of the prefill product (K = 4096)
+    a = inputs.bf16_bits_to_f32(inputs.prefill_activation()[:128])
+    ac, as_, asg = oracle.quantize(a, threads=cores)
+    wc, ws_, wsg = c[:1024], s[:1024], sg
+    t = time.perf_counter()
+    oracle.dot_w4a4(ac, as_, asg, wc, ws_, wsg, 4096, threads=cores)
+    dt = time.perf_counter() - t
+    flops = 2.0 * 128 * 1024 * 4096
+    mfrac = flops / dt / MFMA16_PEAK
+    res["gemm_GFLOP_s"] = flops / dt / 1e9
+    value = 100.0 * (qfrac + gfrac + mfrac) / 3
+    return {"value": value, "unit": "% of MI355X peak (same formula as value)", "cores": cores, "kind": "oracle",
+            "sample": "absmax quantize of the 4096x4096 fp32 q tensor (with amax), MSE of 256x4096, "
+                      "W4A16 M=1 x 4096x4096 weight, W4A4 128x1024 outputs of the prefill product (K=4096)",
+            "components": {k: round(v, 4) for k, v in res.items()}}
+
+
+if __name__ == "__main__":
+    main()

@@ -150,15 +150,17 @@ int nvfp4_gemv_w4a16(const void* x, const uint8_t* w_codes, const uint8_t* w_sca
 }
 
 int nvfp4_gemm_w4a4(const void* a, const float* a_global, const uint8_t* w_codes, const uint8_t* w_scales,
-                    const float* w_global, int64_t M, int64_t N, int64_t K, void* y, int y_dtype, void* workspace,
-                    size_t ws_bytes, void* stream) {
-  if (!a || !w_codes || !w_scales || !w_global || !y || !workspace) return NVFP4_ERR_NULL;
+                    const float* w_global, int64_t M, int64_t N, int64_t K, void* y, int y_dtype, int flags,
+                    void* workspace, size_t ws_bytes, void* stream) {
+  const bool reuse = (flags & NVFP4_GEMM_REUSE_ACT) != 0;
+  if ((!a && !reuse) || !w_codes || !w_scales || !w_global || !y || !workspace) return NVFP4_ERR_NULL;
+  if (flags & ~1) return NVFP4_ERR_FLAGS;
   if (y_dtype != NVFP4_F32 && y_dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
   if (M < 0 || N < 0 || K < 0 || !mul_ok(M, K) || !mul_ok(N, K) || !mul_ok(M, N)) return NVFP4_ERR_SHAPE;
   if (K % 16 != 0) return NVFP4_ERR_SHAPE;
   if (K % 64 != 0 || K == 0 || M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > (int64_t)1 << 30)
     return NVFP4_ERR_UNSUPPORTED;
-  if (!aligned(a, 16) || !aligned(w_codes, 16) || !aligned(w_scales, 4) || !aligned(w_global, 4) ||
+  if ((!reuse && !aligned(a, 16)) || !aligned(w_codes, 16) || !aligned(w_scales, 4) || !aligned(w_global, 4) ||
       (a_global && !aligned(a_global, 4)) || !aligned(y, 16) || !aligned(workspace, 256))
     return NVFP4_ERR_ALIGN;
   if (ws_bytes < gemm_ws_bytes(M, K)) return NVFP4_ERR_WORKSPACE;
@@ -169,15 +171,17 @@ int nvfp4_gemm_w4a4(const void* a, const float* a_global, const uint8_t* w_codes
   uint16_t* a_hat = reinterpret_cast<uint16_t*>(ws + 256);
   float* partials = reinterpret_cast<float*>(ws + 256 + round256((size_t)M * K * 2));
   clear_error();
-  hipError_t e = hipSuccess;
-  if (a_global) {
-    e = hipMemcpyAsync(sga, a_global, sizeof(float), hipMemcpyDeviceToDevice, s);
-  } else {
-    e = launch_global_scale(a, true, M * K, partials, sga, s);
+  if (!reuse) {
+    hipError_t e = hipSuccess;
+    if (a_global) {
+      e = hipMemcpyAsync(sga, a_global, sizeof(float), hipMemcpyDeviceToDevice, s);
+    } else {
+      e = launch_global_scale(a, true, M * K, partials, sga, s);
+    }
+    if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
+    e = launch_act_quant_f16(reinterpret_cast<const uint16_t*>(a), M * K, sga, a_hat, s);
+    if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
   }
-  if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
-  e = launch_act_quant_f16(reinterpret_cast<const uint16_t*>(a), M * K, sga, a_hat, s);
-  if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
   return launch_status(
       launch_gemm_w4a4(a_hat, sga, w_codes, w_scales, w_global, M, N, K, y, y_dtype == NVFP4_BF16, s));
 }

@@ -17,6 +17,7 @@ OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_WORKSPACE, ERR_UNSUPPORTED, E
 F32, BF16 = 0, 1
 GLOBAL_COMPUTE, GLOBAL_GIVEN = 0, 1
 OP_QUANTIZE, OP_GEMM_W4A4, OP_GEMV_W4A16 = 0, 1, 2
+GEMM_QUANTIZE_ACT, GEMM_REUSE_ACT = 0, 1
 
 # name -> (restype, argtypes); mirrors include/nvfp4.h
 _P, _I, _I64, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
@@ -25,7 +26,7 @@ SIGNATURES = {
     "nvfp4_quantize_mse": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _I, _P, _SZ, _P]),
     "nvfp4_dequant": (_I, [_P, _P, _P, _I64, _I64, _P, _I, _P]),
     "nvfp4_gemv_w4a16": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _SZ, _P]),
-    "nvfp4_gemm_w4a4": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _SZ, _P]),
+    "nvfp4_gemm_w4a4": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _I, _P, _SZ, _P]),
     "nvfp4_workspace_bytes": (_SZ, [_I, _I64, _I64]),
     "nvfp4_status_string": (ctypes.c_char_p, [_I]),
     "nvfp4_version": (_I, []),
@@ -180,23 +181,27 @@ def gemv_w4a16(x, w_codes, w_scales, w_global, out_dtype=torch.bfloat16, workspa
 
 
 def gemm_w4a4(a, w_codes, w_scales, w_global, a_global=None, out_dtype=torch.bfloat16, workspace=None,
-              out=None):
+              out=None, reuse_act=False):
     """y = quant(a) W^T with per-call NVFP4 quantization of bf16 a [M, K].
 
     a_global=None computes the activation's tensor scale on the device.
     The workspace (returned contents documented in include/nvfp4.h) may be
-    passed in to inspect the quantized activation."""
+    passed in to inspect the quantized activation; reuse_act=True multiplies
+    the activation already quantized in `workspace` (same a) without
+    quantizing it again."""
     _need_cuda(a, w_codes, w_scales, w_global, a_global)
     if a.dtype != torch.bfloat16 or a.dim() != 2:
         raise ValueError("a must be a 2-D bfloat16 tensor")
     M, K = a.shape
     N = _check_weight(w_codes, w_scales, K)
+    if reuse_act and workspace is None:
+        raise ValueError("reuse_act needs the workspace of the call that quantized the activation")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a.device)
     ws = workspace if workspace is not None else _alloc_ws(workspace_bytes(OP_GEMM_W4A4, M, K), a.device)
     st = lib().nvfp4_gemm_w4a4(_ptr(a), _ptr(a_global), _ptr(w_codes), _ptr(w_scales), _ptr(w_global), M, N, K,
-                               _ptr(out), _dtype_code(out.dtype), _ptr(ws), 0 if ws is None else ws.numel(),
-                               _stream())
+                               _ptr(out), _dtype_code(out.dtype), GEMM_REUSE_ACT if reuse_act else GEMM_QUANTIZE_ACT,
+                               _ptr(ws), 0 if ws is None else ws.numel(), _stream())
     _check("nvfp4_gemm_w4a4", st)
     return out
 

@@ -70,6 +70,9 @@ typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1 } nvfp4_dtype;
 /* flags for the quantizers (bit 0) */
 enum { NVFP4_GLOBAL_COMPUTE = 0, NVFP4_GLOBAL_GIVEN = 1 };
 
+/* flags for nvfp4_gemm_w4a4 (bit 0) */
+enum { NVFP4_GEMM_QUANTIZE_ACT = 0, NVFP4_GEMM_REUSE_ACT = 1 };
+
 /* operation ids for nvfp4_workspace_bytes */
 enum { NVFP4_OP_QUANTIZE = 0, NVFP4_OP_GEMM_W4A4 = 1, NVFP4_OP_GEMV_W4A16 = 2 };
 
@@ -156,12 +159,18 @@ int nvfp4_gemv_w4a16(const void* x, const uint8_t* w_codes, const uint8_t* w_sca
  *                           (exact: <= 6 significant bits, magnitudes in
  *                           [2^-10, 2688]), i.e. the quantized activation
  *              after that   amax partials (unspecified)
+ *   flags    NVFP4_GEMM_QUANTIZE_ACT: quantize `a` into the workspace, then
+ *            multiply; NVFP4_GEMM_REUSE_ACT: the workspace already holds the
+ *            quantized activation of the same [M, K] input from an earlier
+ *            call on this stream (several weights sharing one input, e.g.
+ *            q/k/v or gate/up projections): only the product runs, and `a`
+ *            and `a_global` are not read.
  *   y[m, n] = round(fp32(s_gA * s_gW) * sum_k (q_a s_a)[m,k] (q_w s_w)[n,k])
  *   with the products exact and the sum accumulated in fp32.
  */
 int nvfp4_gemm_w4a4(const void* a, const float* a_global, const uint8_t* w_codes,
                     const uint8_t* w_scales, const float* w_global,
-                    int64_t M, int64_t N, int64_t K, void* y, int y_dtype,
+                    int64_t M, int64_t N, int64_t K, void* y, int y_dtype, int flags,
                     void* workspace, size_t ws_bytes, void* stream);
 
 /* Workspace size in bytes for an operation: NVFP4_OP_QUANTIZE with

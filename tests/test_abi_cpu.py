@@ -95,14 +95,17 @@ def test_gemm_validation():
     L = nv.lib()
     f = L.nvfp4_gemm_w4a4
     W = 1 << 30
-    assert f(None, None, A16, A16, A4, 64, 64, 64, A16, nv.BF16, A16, W, None) == nv.ERR_NULL
-    assert f(A16, None, A16, A16, A4, 64, 64, 64, A16, nv.BF16, None, W, None) == nv.ERR_NULL
-    assert f(A16, None, A16, A16, A4, 64, 64, 64, A16, 9, A16, W, None) == nv.ERR_DTYPE
-    assert f(A16, None, A16, A16, A4, 64, 64, 40, A16, nv.BF16, A16, W, None) == nv.ERR_SHAPE
-    assert f(A16, None, A16, A16, A4, 64, 64, 96, A16, nv.BF16, A16, W, None) == nv.ERR_UNSUPPORTED
-    assert f(A16, None, A16, A16, A4, 64, 64, 64, A16, nv.BF16, A16 + 16, W, None) == nv.ERR_ALIGN
-    assert f(A16, None, A16, A16, A4, 64, 64, 64, A16, nv.BF16, A16, 16, None) == nv.ERR_WORKSPACE
-    assert f(A16, None, A16, A16, A4, 0, 64, 64, A16, nv.BF16, A16, W, None) == nv.OK
+    Q, R = nv.GEMM_QUANTIZE_ACT, nv.GEMM_REUSE_ACT
+    assert f(None, None, A16, A16, A4, 64, 64, 64, A16, nv.BF16, Q, A16, W, None) == nv.ERR_NULL
+    assert f(A16, None, A16, A16, A4, 64, 64, 64, A16, nv.BF16, Q, None, W, None) == nv.ERR_NULL
+    assert f(A16, None, A16, A16, A4, 64, 64, 64, A16, 9, Q, A16, W, None) == nv.ERR_DTYPE
+    assert f(A16, None, A16, A16, A4, 64, 64, 64, A16, nv.BF16, 6, A16, W, None) == nv.ERR_FLAGS
+    assert f(A16, None, A16, A16, A4, 64, 64, 40, A16, nv.BF16, Q, A16, W, None) == nv.ERR_SHAPE
+    assert f(A16, None, A16, A16, A4, 64, 64, 96, A16, nv.BF16, Q, A16, W, None) == nv.ERR_UNSUPPORTED
+    assert f(A16, None, A16, A16, A4, 64, 64, 64, A16, nv.BF16, Q, A16 + 16, W, None) == nv.ERR_ALIGN
+    assert f(A16, None, A16, A16, A4, 64, 64, 64, A16, nv.BF16, Q, A16, 16, None) == nv.ERR_WORKSPACE
+    assert f(A16, None, A16, A16, A4, 0, 64, 64, A16, nv.BF16, Q, A16, W, None) == nv.OK
+    assert f(None, None, A16, A16, A4, 0, 64, 64, A16, nv.BF16, R, A16, W, None) == nv.OK  # reuse: a unused
 
 
 def test_python_layer_rejects_mismatched_packed_shapes():

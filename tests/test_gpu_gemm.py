@@ -99,6 +99,9 @@ def _check_gemm(ab, w_c, w_s, w_g, pairs=None, a_global=None, what=""):
     assert_within_tau(host(y32)[sel].reshape(-1), ystar, tau, what + " fp32")
     yb = nv.gemm_w4a4(a_dev, w_c, w_s, w_g, a_global=ag, workspace=ws)
     assert_bracket_bf16(host(yb)[sel].reshape(-1), ystar, tau, what + " bf16")
+    # the same product again from the activation already in the workspace
+    yr = nv.gemm_w4a4(a_dev, w_c, w_s, w_g, workspace=ws, reuse_act=True)
+    assert np.array_equal(host(yr), host(yb))
 
 
 @pytest.mark.parametrize("mnk", [(1, 64, 64), (70, 130, 192), (300, 520, 512), (257, 300, 4096)])
