@@ -157,11 +157,9 @@ def main():
             for M in (1, 4, 16):
                 xm = xb[:M].contiguous()
                 ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(GEMV_COPIES)]
-                ws = torch.empty(max(nv.workspace_bytes(nv.OP_GEMV_W4A16, M, N), 256), dtype=torch.uint8, device=dev)
-
-                def run(copies=copies, xm=xm, ys=ys, ws=ws, g=g):
+                def run(copies=copies, xm=xm, ys=ys, g=g):
                     for (cc, ss), y in zip(copies, ys):
-                        nv.gemv_w4a16(xm, cc, ss, g, workspace=ws, out=y)
+                        nv.gemv_w4a16(xm, cc, ss, g, out=y)
 
                 nbytes = GEMV_COPIES * (N * K * 0.5625 + 2 * M * K + 2 * M * N)
                 capture(f"gemv_{N}x{K}_M{M}", run, nbytes=nbytes, flops=GEMV_COPIES * 2.0 * M * N * K,

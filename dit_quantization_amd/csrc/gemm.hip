@@ -96,28 +96,31 @@ __device__ __forceinline__ f16x8 unpack8_f16(uint32_t c, f16x2 s2) {
   return r;
 }
 
-__device__ __forceinline__ f16x2 e4m3_to_f16x2(uint32_t b) {
-  _Float16 h = (_Float16)e4m3_to_f32(b);
-  return f16x2{h, h};
+// Two E4M3 scale bytes (bits 0..15) -> fp16 values (exact: every E4M3 value,
+// subnormals included, is a normal fp16 number).
+__device__ __forceinline__ f16x2 e4m3x2_to_f16x2(uint32_t b) {
+  return f16x2{(_Float16)e4m3_to_f32(b & 0xFFu), (_Float16)e4m3_to_f32((b >> 8) & 0xFFu)};
 }
 
-// BM x BN tile per workgroup, 4 waves in 2x2; each wave (BM/2) x (BN/2) as
-// TM x TN tiles of 32x32.  grid.x enumerates tiles (XCD-aware order).
-template <int BM, int BN>
-__global__ __launch_bounds__(256, 1) void gemm_w4a4_kernel(const uint16_t* __restrict__ a_hat,
-                                                           const float* __restrict__ sga_ptr,
-                                                           const uint8_t* __restrict__ codes,
-                                                           const uint8_t* __restrict__ scales,
-                                                           const float* __restrict__ sgw_ptr, int M, int N, int K,
-                                                           void* __restrict__ y, int bf16_out) {
-  constexpr int TM = BM / 64, TN = BN / 64;              // 32x32 tiles per wave
+// BM x BN tile per workgroup of WM x WN waves; each wave (BM/WM) x (BN/WN)
+// as TM x TN tiles of 32x32.  grid.x enumerates tiles (XCD-aware order).
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_w4a4_kernel(const uint16_t* __restrict__ a_hat,
+                                                                 const float* __restrict__ sga_ptr,
+                                                                 const uint8_t* __restrict__ codes,
+                                                                 const uint8_t* __restrict__ scales,
+                                                                 const float* __restrict__ sgw_ptr, int M, int N,
+                                                                 int K, void* __restrict__ y, int bf16_out) {
+  constexpr int NT = WM * WN * 64;                       // threads
+  constexpr int TM = BM / WM / 32, TN = BN / WN / 32;    // 32x32 tiles per wave
   constexpr int A_CHUNKS = BM * BK * 2 / 16;             // 16-byte chunks per A tile
-  constexpr int A_PER_THREAD = A_CHUNKS / 256;
+  constexpr int A_PER_THREAD = A_CHUNKS / NT;
+  static_assert(A_CHUNKS % NT == 0, "A tile must split evenly over the threads");
   __shared__ __attribute__((aligned(16))) u32x4 lds_a[2][A_CHUNKS];
 
   // Tile coordinates.  Consecutive workgroup ids go to different XCDs
-  // (round robin over 8); remap so that each XCD receives a contiguous run
-  // of tiles, which then share A rows / W rows in that XCD's L2.
+  // (round robin over 8); remap so each XCD receives a contiguous run of
+  // tiles, which then share A rows / W rows in that XCD's L2.
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const int ntiles = tiles_m * tiles_n;
   int bid = blockIdx.x;
@@ -136,26 +139,28 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a4_kernel(const uint16_t* __res
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int l32 = lane & 31, g = lane >> 5;  // MFMA row/col and k lane group
 
-  // ---- A global -> LDS mapping: chunk i = tid + 256 j -> row i / 8, chunk i % 8
-  const u32x4* a_rows[A_PER_THREAD];
+  // ---- A global -> LDS mapping: chunk i = tid + NT j -> row i / 8, chunk i % 8
+  int64_t a_off[A_PER_THREAD];
+  int a_slot[A_PER_THREAD];
 #pragma unroll
   for (int j = 0; j < A_PER_THREAD; ++j) {
-    int i = tid + 256 * j;
+    int i = tid + NT * j;
     int r = i >> 3, c = i & 7;
     int gr = min(m0 + r, M - 1);
-    a_rows[j] = reinterpret_cast<const u32x4*>(a_hat + (int64_t)gr * K) + c;
+    a_off[j] = (int64_t)gr * (K / 8) + c;   // in 16-byte chunks
+    a_slot[j] = r * 8 + (c ^ (r & 7));
   }
-  auto lds_slot = [](int r, int c) { return r * 8 + (c ^ (r & 7)); };
+  const u32x4* a_base = reinterpret_cast<const u32x4*>(a_hat);
 
-  // ---- W rows of this lane: TN sub-tiles, row n0 + wn*(BN/2) + 32 t + l32
+  // ---- W rows of this lane: TN sub-tiles, row n0 + wn*(BN/WN) + 32 t + l32
   const uint8_t* wc[TN];
   const uint8_t* wsc[TN];
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
-    int n = min(n0 + wn * (BN / 2) + 32 * t + l32, N - 1);
+    int n = min(n0 + wn * (BN / WN) + 32 * t + l32, N - 1);
     wc[t] = codes + (int64_t)n * (K / 2) + 16 * g;      // 32 codes = 16 bytes per K step
     wsc[t] = scales + (int64_t)n * (K / 16) + 2 * g;    // 2 scale bytes per K step
   }
@@ -173,67 +178,65 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a4_kernel(const uint16_t* __res
   u32x4 wreg[TN];
   uint32_t sreg[TN];
 
-  // prologue: stage 0
+  // prologue: K step 0 -> LDS buffer 0 and W registers
 #pragma unroll
-  for (int j = 0; j < A_PER_THREAD; ++j) areg[j] = a_rows[j][0];
+  for (int j = 0; j < A_PER_THREAD; ++j) areg[j] = a_base[a_off[j]];
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
     wreg[t] = *reinterpret_cast<const u32x4*>(wc[t]);
     sreg[t] = *reinterpret_cast<const uint16_t*>(wsc[t]);
   }
 #pragma unroll
-  for (int j = 0; j < A_PER_THREAD; ++j) {
-    int i = tid + 256 * j;
-    lds_a[0][lds_slot(i >> 3, i & 7)] = areg[j];
-  }
+  for (int j = 0; j < A_PER_THREAD; ++j) lds_a[0][a_slot[j]] = areg[j];
 
   for (int kt = 0; kt < KT; ++kt) {
     const int buf = kt & 1;
     __syncthreads();
-    // prefetch the next K step
+    // issue the loads of the next K step before any math of this one
     u32x4 wnext[TN];
     uint32_t snext[TN];
-    const bool more = kt + 1 < KT;
-    if (more) {
-      const int koff = (kt + 1) * BK;
+    const int kn = min(kt + 1, KT - 1);
 #pragma unroll
-      for (int j = 0; j < A_PER_THREAD; ++j) areg[j] = a_rows[j][koff / 8];
+    for (int j = 0; j < A_PER_THREAD; ++j) areg[j] = a_base[a_off[j] + kn * (BK / 8)];
 #pragma unroll
-      for (int t = 0; t < TN; ++t) {
-        wnext[t] = *reinterpret_cast<const u32x4*>(wc[t] + koff / 2);
-        snext[t] = *reinterpret_cast<const uint16_t*>(wsc[t] + koff / 16);
-      }
+    for (int t = 0; t < TN; ++t) {
+      wnext[t] = *reinterpret_cast<const u32x4*>(wc[t] + kn * (BK / 2));
+      snext[t] = *reinterpret_cast<const uint16_t*>(wsc[t] + kn * (BK / 16));
     }
+    __builtin_amdgcn_sched_barrier(0);
     // compute on the current K step: 4 sub-steps of 16
+    f16x2 sc0[TN], sc1[TN];
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+      f16x2 s2 = e4m3x2_to_f16x2(sreg[t]);
+      sc0[t] = f16x2{s2.x, s2.x};
+      sc1[t] = f16x2{s2.y, s2.y};
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      f16x8 bfrag[TN];
-#pragma unroll
-      for (int t = 0; t < TN; ++t) {
-        uint32_t sb = (s < 2) ? (sreg[t] & 0xFFu) : (sreg[t] >> 8);
-        bfrag[t] = unpack8_f16(wreg[t][s], e4m3_to_f16x2(sb));
-      }
+      f16x8 afrag[TM];
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        int r = wm * (BM / 2) + 32 * i + l32;
-        u32x4 av = lds_a[buf][lds_slot(r, 4 * g + s)];
-        f16x8 afrag = __builtin_bit_cast(f16x8, av);
+        int r = wm * (BM / WM) + 32 * i + l32;
+        afrag[i] = __builtin_bit_cast(f16x8, lds_a[buf][r * 8 + ((4 * g + s) ^ (r & 7))]);
+      }
+      f16x8 bfrag[TN];
+#pragma unroll
+      for (int t = 0; t < TN; ++t) bfrag[t] = unpack8_f16(wreg[t][s], s < 2 ? sc0[t] : sc1[t]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int t = 0; t < TN; ++t)
-          acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afrag, bfrag[t], acc[i][t], 0, 0, 0);
-      }
+          acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afrag[i], bfrag[t], acc[i][t], 0, 0, 0);
     }
-    if (more) {
+    __builtin_amdgcn_sched_barrier(0);
+    // stage the next K step
 #pragma unroll
-      for (int j = 0; j < A_PER_THREAD; ++j) {
-        int i = tid + 256 * j;
-        lds_a[buf ^ 1][lds_slot(i >> 3, i & 7)] = areg[j];
-      }
+    for (int j = 0; j < A_PER_THREAD; ++j) lds_a[buf ^ 1][a_slot[j]] = areg[j];
 #pragma unroll
-      for (int t = 0; t < TN; ++t) {
-        wreg[t] = wnext[t];
-        sreg[t] = snext[t];
-      }
+    for (int t = 0; t < TN; ++t) {
+      wreg[t] = wnext[t];
+      sreg[t] = snext[t];
     }
   }
 
@@ -243,11 +246,11 @@ __global__ __launch_bounds__(256, 1) void gemm_w4a4_kernel(const uint16_t* __res
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
-      const int n = n0 + wn * (BN / 2) + 32 * t + l32;
+      const int n = n0 + wn * (BN / WN) + 32 * t + l32;
       if (n >= N) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * (BM / 2) + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
+        const int m = m0 + wm * (BM / WM) + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
         if (m >= M) continue;
         float v = acc[i][t][r] * alpha;
         if (bf16_out)
@@ -264,12 +267,12 @@ hipError_t launch_gemm_w4a4(const uint16_t* a_hat, const float* sga, const uint8
                             hipStream_t stream) {
   int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
   if (big >= 256) {
-    hipLaunchKernelGGL((gemm_w4a4_kernel<256, 256>), dim3((unsigned)big), dim3(256), 0, stream, a_hat, sga, codes,
-                       scales, sgw, (int)M, (int)N, (int)K, y, bf16_out ? 1 : 0);
+    hipLaunchKernelGGL((gemm_w4a4_kernel<256, 256, 2, 4>), dim3((unsigned)big), dim3(512), 0, stream, a_hat, sga,
+                       codes, scales, sgw, (int)M, (int)N, (int)K, y, bf16_out ? 1 : 0);
   } else {
     int64_t small = ((M + 127) / 128) * ((N + 127) / 128);
-    hipLaunchKernelGGL((gemm_w4a4_kernel<128, 128>), dim3((unsigned)small), dim3(256), 0, stream, a_hat, sga, codes,
-                       scales, sgw, (int)M, (int)N, (int)K, y, bf16_out ? 1 : 0);
+    hipLaunchKernelGGL((gemm_w4a4_kernel<128, 128, 2, 2>), dim3((unsigned)small), dim3(256), 0, stream, a_hat, sga,
+                       codes, scales, sgw, (int)M, (int)N, (int)K, y, bf16_out ? 1 : 0);
   }
   return hipGetLastError();
 }

@@ -18,10 +18,8 @@ hipError_t launch_quantize_mse(const void* x, bool bf16, int64_t n_elems, const 
                                uint8_t* scales, hipStream_t stream);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* sg, int64_t n_elems,
                           void* out, bool bf16_out, hipStream_t stream);
-size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemv_w4a16(const uint16_t* x, const uint8_t* codes, const uint8_t* scales, const float* sg,
-                             int64_t M, int64_t N, int64_t K, void* y, bool bf16_out, float* partial,
-                             hipStream_t stream);
+                             int64_t M, int64_t N, int64_t K, void* y, bool bf16_out, hipStream_t stream);
 hipError_t launch_act_quant_f16(const uint16_t* a, int64_t n_elems, const float* sg, uint16_t* a_hat,
                                 hipStream_t stream);
 hipError_t launch_gemm_w4a4(const uint16_t* a_hat, const float* sga, const uint8_t* codes, const uint8_t* scales,

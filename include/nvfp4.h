@@ -130,9 +130,9 @@ int nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const float* glob
  *   y[m, n] = s_gW * sum_k x[m, k] * q[n, k] * s_b[n, k/16]
  *   x        [M, K] bf16;  w_codes [N, K/2];  w_scales [N, K/16];
  *   w_global 1 device fp32; y [M, N] of y_dtype (NVFP4_BF16 or NVFP4_F32)
- *   workspace >= nvfp4_workspace_bytes(NVFP4_OP_GEMV_W4A16, M, N) bytes,
- *            16-byte aligned: fp32 partial sums when the K range is split
- *            across workgroups (contents on return unspecified)
+ *   workspace reserved: this version needs none
+ *            (nvfp4_workspace_bytes(NVFP4_OP_GEMV_W4A16, M, N) returns 0);
+ *            may be NULL
  *   0 <= M <= 16 (the decode batch; M = 0 or N = 0 is a no-op); fp32
  *   accumulation, fp32 epilogue (x s_gW), round-to-nearest-even bf16 output.
  */
