@@ -96,16 +96,21 @@ __device__ __forceinline__ f16x8 unpack8_f16(uint32_t c, f16x2 s2) {
   return r;
 }
 
-// Two E4M3 scale bytes (bits 0..15) -> fp16 values (exact: every E4M3 value,
-// subnormals included, is a normal fp16 number).
+// Two E4M3 scale bytes (bits 0..15) -> fp16 values with the hardware
+// converter (exact: every E4M3 value, subnormals included, is a normal fp16
+// number; the E4M3 decode is checked exhaustively by the dequant tests).
 __device__ __forceinline__ f16x2 e4m3x2_to_f16x2(uint32_t b) {
-  return f16x2{(_Float16)e4m3_to_f32(b & 0xFFu), (_Float16)e4m3_to_f32((b >> 8) & 0xFFu)};
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false);
 }
 
 // BM x BN tile per workgroup of WM x WN waves; each wave (BM/WM) x (BN/WN)
 // as TM x TN tiles of 32x32.  grid.x enumerates tiles (XCD-aware order).
+// K loop: A tiles are double buffered in LDS and fetched two K steps ahead
+// into one of two register sets; packed weights are fetched two K steps
+// ahead into registers.  The loop is unrolled by two so every register set
+// is addressed statically.
 template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_w4a4_kernel(const uint16_t* __restrict__ a_hat,
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2))) void gemm_w4a4_kernel(const uint16_t* __restrict__ a_hat,
                                                                  const float* __restrict__ sga_ptr,
                                                                  const uint8_t* __restrict__ codes,
                                                                  const uint8_t* __restrict__ scales,
@@ -114,7 +119,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_w4a4_kernel(const uint16_t*
   constexpr int NT = WM * WN * 64;                       // threads
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;    // 32x32 tiles per wave
   constexpr int A_CHUNKS = BM * BK * 2 / 16;             // 16-byte chunks per A tile
-  constexpr int A_PER_THREAD = A_CHUNKS / NT;
+  constexpr int APT = A_CHUNKS / NT;
   static_assert(A_CHUNKS % NT == 0, "A tile must split evenly over the threads");
   __shared__ __attribute__((aligned(16))) u32x4 lds_a[2][A_CHUNKS];
 
@@ -142,18 +147,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_w4a4_kernel(const uint16_t*
   const int wm = wave / WN, wn = wave % WN;
   const int l32 = lane & 31, g = lane >> 5;  // MFMA row/col and k lane group
 
-  // ---- A global -> LDS mapping: chunk i = tid + NT j -> row i / 8, chunk i % 8
-  int64_t a_off[A_PER_THREAD];
-  int a_slot[A_PER_THREAD];
-#pragma unroll
-  for (int j = 0; j < A_PER_THREAD; ++j) {
-    int i = tid + NT * j;
-    int r = i >> 3, c = i & 7;
-    int gr = min(m0 + r, M - 1);
-    a_off[j] = (int64_t)gr * (K / 8) + c;   // in 16-byte chunks
-    a_slot[j] = r * 8 + (c ^ (r & 7));
-  }
-  const u32x4* a_base = reinterpret_cast<const u32x4*>(a_hat);
+  // ---- A global -> LDS mapping: chunk tid + NT j -> row tid / 8 + j NT / 8,
+  // 16-byte chunk tid % 8 of the row's 64 k; LDS slot XOR-swizzled by row.
+  // NT / 8 is a multiple of 8, so every row of a thread has the same swizzle.
+  const int a_r0 = tid >> 3, a_c = tid & 7;
+  const int a_slot0 = a_r0 * 8 + (a_c ^ (a_r0 & 7));
+  const u32x4* a_base = reinterpret_cast<const u32x4*>(a_hat) + a_c;
 
   // ---- W rows of this lane: TN sub-tiles, row n0 + wn*(BN/WN) + 32 t + l32
   const uint8_t* wc[TN];
@@ -174,41 +173,35 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_w4a4_kernel(const uint16_t*
       for (int r = 0; r < 16; ++r) acc[i][t][r] = 0.0f;
 
   const int KT = K / BK;
-  u32x4 areg[A_PER_THREAD];
-  u32x4 wreg[TN];
-  uint32_t sreg[TN];
-
-  // prologue: K step 0 -> LDS buffer 0 and W registers
+  u32x4 aset0[APT], aset1[APT];
+  u32x4 wset0[TN], wset1[TN];
+  uint32_t sset0[TN], sset1[TN];
+  auto load_a = [&](u32x4 (&dst)[APT], int kt) {
+    const int kk = min(kt, KT - 1) * (BK / 8);
 #pragma unroll
-  for (int j = 0; j < A_PER_THREAD; ++j) areg[j] = a_base[a_off[j]];
-#pragma unroll
-  for (int t = 0; t < TN; ++t) {
-    wreg[t] = *reinterpret_cast<const u32x4*>(wc[t]);
-    sreg[t] = *reinterpret_cast<const uint16_t*>(wsc[t]);
-  }
-#pragma unroll
-  for (int j = 0; j < A_PER_THREAD; ++j) lds_a[0][a_slot[j]] = areg[j];
-
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    __syncthreads();
-    // issue the loads of the next K step before any math of this one
-    u32x4 wnext[TN];
-    uint32_t snext[TN];
-    const int kn = min(kt + 1, KT - 1);
-#pragma unroll
-    for (int j = 0; j < A_PER_THREAD; ++j) areg[j] = a_base[a_off[j] + kn * (BK / 8)];
+    for (int j = 0; j < APT; ++j) {
+      const int row = min(m0 + a_r0 + j * (NT / 8), M - 1);
+      dst[j] = a_base[(int64_t)row * (K / 8) + kk];
+    }
+  };
+  auto load_w = [&](u32x4 (&dw)[TN], uint32_t (&ds)[TN], int kt) {
+    const int kk = min(kt, KT - 1);
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
-      wnext[t] = *reinterpret_cast<const u32x4*>(wc[t] + kn * (BK / 2));
-      snext[t] = *reinterpret_cast<const uint16_t*>(wsc[t] + kn * (BK / 16));
+      dw[t] = *reinterpret_cast<const u32x4*>(wc[t] + kk * (BK / 2));
+      ds[t] = *reinterpret_cast<const uint16_t*>(wsc[t] + kk * (BK / 16));
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // compute on the current K step: 4 sub-steps of 16
+  };
+  auto store_a = [&](const u32x4 (&src)[APT], int buf) {
+#pragma unroll
+    for (int j = 0; j < APT; ++j) lds_a[buf][a_slot0 + j * NT] = src[j];
+  };
+  // one K step of 64 = 4 sub-steps of 16 from LDS buffer `buf`
+  auto compute = [&](int buf, const u32x4 (&wr)[TN], const uint32_t (&sr)[TN]) {
     f16x2 sc0[TN], sc1[TN];
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
-      f16x2 s2 = e4m3x2_to_f16x2(sreg[t]);
+      f16x2 s2 = e4m3x2_to_f16x2(sr[t]);
       sc0[t] = f16x2{s2.x, s2.x};
       sc1[t] = f16x2{s2.y, s2.y};
     }
@@ -222,21 +215,53 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_w4a4_kernel(const uint16_t*
       }
       f16x8 bfrag[TN];
 #pragma unroll
-      for (int t = 0; t < TN; ++t) bfrag[t] = unpack8_f16(wreg[t][s], s < 2 ? sc0[t] : sc1[t]);
+      for (int t = 0; t < TN; ++t) bfrag[t] = unpack8_f16(wr[t][s], s < 2 ? sc0[t] : sc1[t]);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int t = 0; t < TN; ++t)
           acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afrag[i], bfrag[t], acc[i][t], 0, 0, 0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // stage the next K step
+  };
+
+  // prologue: A(0) -> LDS buffer 0; A(1) in flight in aset0; W(0), W(1) in flight
+  load_a(aset1, 0);
+  load_w(wset0, sset0, 0);
+  load_w(wset1, sset1, 1);
+  store_a(aset1, 0);
+  load_a(aset0, 1);
+  for (int kt = 0; kt < KT; kt += 2) {
+    {  // even step: LDS 0 holds A(kt); aset0 = A(kt+1); wset0 = W(kt)
+      __syncthreads();
+      u32x4 wcur[TN];
+      uint32_t scur[TN];
 #pragma unroll
-    for (int j = 0; j < A_PER_THREAD; ++j) lds_a[buf ^ 1][a_slot[j]] = areg[j];
+      for (int t = 0; t < TN; ++t) {
+        wcur[t] = wset0[t];
+        scur[t] = sset0[t];
+      }
+      load_a(aset1, kt + 2);
+      load_w(wset0, sset0, kt + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(0, wcur, scur);
+      __builtin_amdgcn_sched_barrier(0);
+      store_a(aset0, 1);
+    }
+    if (kt + 1 < KT) {  // odd step: LDS 1 holds A(kt+1); aset1 = A(kt+2); wset1 = W(kt+1)
+      __syncthreads();
+      u32x4 wcur[TN];
+      uint32_t scur[TN];
 #pragma unroll
-    for (int t = 0; t < TN; ++t) {
-      wreg[t] = wnext[t];
-      sreg[t] = snext[t];
+      for (int t = 0; t < TN; ++t) {
+        wcur[t] = wset1[t];
+        scur[t] = sset1[t];
+      }
+      load_a(aset0, kt + 3);
+      load_w(wset1, sset1, kt + 3);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(1, wcur, scur);
+      __builtin_amdgcn_sched_barrier(0);
+      store_a(aset1, 0);
     }
   }
 
@@ -265,14 +290,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_w4a4_kernel(const uint16_t*
 hipError_t launch_gemm_w4a4(const uint16_t* a_hat, const float* sga, const uint8_t* codes, const uint8_t* scales,
                             const float* sgw, int64_t M, int64_t N, int64_t K, void* y, bool bf16_out,
                             hipStream_t stream) {
-  int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
-  if (big >= 256) {
-    hipLaunchKernelGGL((gemm_w4a4_kernel<256, 256, 2, 4>), dim3((unsigned)big), dim3(512), 0, stream, a_hat, sga,
-                       codes, scales, sgw, (int)M, (int)N, (int)K, y, bf16_out ? 1 : 0);
+  // 256 x 256 tiles (8 waves, 128 x 64 per wave) whenever they cover at least
+  // half of the 256 CUs; otherwise 128 x 128 tiles (4 waves) for more
+  // parallelism on short activations (measured on the prefill and DiT shapes).
+  const int b = bf16_out ? 1 : 0;
+  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+  if (t256 >= 128) {
+    hipLaunchKernelGGL((gemm_w4a4_kernel<256, 256, 2, 4>), dim3((unsigned)t256), dim3(512), 0, stream, a_hat, sga,
+                       codes, scales, sgw, (int)M, (int)N, (int)K, y, b);
   } else {
-    int64_t small = ((M + 127) / 128) * ((N + 127) / 128);
-    hipLaunchKernelGGL((gemm_w4a4_kernel<128, 128, 2, 2>), dim3((unsigned)small), dim3(256), 0, stream, a_hat, sga,
-                       codes, scales, sgw, (int)M, (int)N, (int)K, y, bf16_out ? 1 : 0);
+    const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+    hipLaunchKernelGGL((gemm_w4a4_kernel<128, 128, 2, 2>), dim3((unsigned)t128), dim3(256), 0, stream, a_hat, sga,
+                       codes, scales, sgw, (int)M, (int)N, (int)K, y, b);
   }
   return hipGetLastError();
 }
