@@ -42,8 +42,38 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--phases", default="quantize,gemv,gemm")
+    p.add_argument("--phases", default="quantize,gemv,gemm",
+                   help="comma list of quantize, gemv, gemm (= prefill + dit), prefill, dit")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                   help="only run a plain device-to-device copy of BYTES (HBM counter calibration) and exit")
     return p.parse_args()
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w4a4_prefill_traffic.json")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for name in ("gemm.hip", "device_common.hpp"):
+        with open(os.path.join(ROOT, "dit_quantization_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per launch of the prefill GEMM kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE runs, or None when the kernel source
+    changed after the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
 
 
 def log(*a):
@@ -83,6 +113,14 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        src = torch.empty(args.copy_calibration, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": args.copy_calibration}), flush=True)
+        return
     phases = set(args.phases.split(","))
     t0 = time.time()
 
@@ -167,7 +205,7 @@ def main():
             del w
 
     # ------------------------------------------------------------ gemm
-    if "gemm" in phases:
+    if "gemm" in phases or "prefill" in phases:
         log("[setup] prefill")
         a = bf16(inputs.prefill_activation())
         wts = {}
@@ -191,6 +229,7 @@ def main():
         capture("gemm_prefill_up_reuse", prefill_up, flops=2.0 * M * N * K,
                 nbytes=M * K * 2 + N * K * 0.5625 + 2 * M * N)
 
+    if "gemm" in phases or "dit" in phases:
         log("[setup] dit block")
         a_img, a_txt, h_img, h_txt = inputs.dit_activations()
         dit_calls = []
@@ -309,7 +348,8 @@ def main():
         t = per[dom]["us"] / 1e6
         if bound == "mfma":
             roofline = {"bound": "mfma", "kernel": kname, "achieved": flops / t / 1e12, "peak": 2500.0,
-                        "unit": "TFLOP/s", "frac": flops / t / MFMA16_PEAK, "traffic": None}
+                        "unit": "TFLOP/s", "frac": flops / t / MFMA16_PEAK, "traffic": stored_traffic(),
+                        "algorithmic_bytes": nbytes}
         elif bound == "alu":
             roofline = {"bound": "alu", "kernel": kname, "achieved": ops / t / 1e12, "peak": VALU_PEAK / 1e12,
                         "unit": "Tops/s", "frac": ops / t / VALU_PEAK, "traffic": None}
