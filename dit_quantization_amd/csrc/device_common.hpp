@@ -146,6 +146,16 @@ __device__ __forceinline__ uint32_t encode8(const float* w, float sb, float sg, 
   return word;
 }
 
+// Raw buffer access (gfx9 buffer resource, stride 0): a load whose byte
+// offset is at or past `bytes` returns zero without touching memory, which
+// replaces clamped addresses and select masks for tails and idle lanes.
+constexpr int kBufOOB = 0x40000000;  // an offset past every buffer the kernels address this way
+constexpr int kBufNT = 2;            // aux bit: non-temporal (streamed once)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_buf(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

@@ -1,34 +1,38 @@
-// W4A16 decode product y = x W^^T for NVFP4 weights and bf16 activations,
+// W4A16 decode product y = x W^T for NVFP4 weights and bf16 activations,
 // M <= 16 rows ("Tu pipeline NVFP4: meter 62 GB de modelo en 24 GB de
 // laptop", section 2: W4A16 stores 4-bit weights and unpacks them to 16 bits
 // for the multiply; decoding reads every weight once per token and is bound
 // by memory bandwidth).
 //
-// Design (gfx950): one workgroup of 8 waves owns 16 weight rows and all of K.
-// K is cut into 32 segments (8 waves x 4 lane groups); lane (n, h) of wave w
-// owns segment 4w + h of row n and issues every 16-byte load of its packed
-// codes and scales up front, so a workgroup keeps its whole share of the
-// weights in flight (about 64 KB per CU), then feeds
-// v_mfma_f32_16x16x32_bf16: B = exact bf16 values q * s_b of its codes
-// (<= 6 significant bits, magnitudes in [2^-10, 2688]), A = the matching
-// x[m, k] (read from L2, double buffered).  Lane groups hold different k
-// ranges but A and B use the same k for the same lane, which is all an MFMA
-// needs.  The 8 waves' fp32 partial tiles are added in LDS in wave order;
-// the fp32 epilogue multiplies by s_g and rounds to bf16 (RNE).  One kernel,
-// no workspace.
+// M > 1 design (gfx950): a workgroup of NW waves owns 16 * T weight rows;
+// its waves split K.  K is read in super-chunks of 128 (4 chunks of 32
+// codes = 16 bytes per row), 4 super-chunks per pass.  Lane (n, g) of a wave
+// (n = lane % 16, g = lane / 16) loads chunk 4s + g of row n, so one load
+// instruction reads 16 rows x 64 contiguous bytes, and unpacks its 4 code
+// dwords to exact bf16 values q * s_b (<= 6 significant bits, magnitudes in
+// [2^-10, 2688]) as the B operands of 4 v_mfma_f32_16x16x32_bf16.  The
+// scales of a pass come from one 8-byte load per lane, redistributed between
+// the 4 lanes of a row with two cross-lane exchanges.  The vector memory
+// pipe bounds this kernel, so the x operand is built from as few load
+// instructions as possible:
+//  * M <= 4 (staggered): lane (4 j + i, g) loads the 8 values of x[i] that
+//    meet MFMA j in lane group g -- one 16-byte load per lane covers all 4
+//    MFMAs of a super-chunk.  MFMA j keeps only the lanes with j' == j, so
+//    output row 4 j + i collects x[i] times the codes of MFMA j, and the
+//    4 row blocks are added across lane groups at the end.
+//  * M > 4 (dense): lane (m, g) holds x[m] on its lane group's k slots for
+//    each MFMA; 4 loads per super-chunk cover 16 rows.
+// Rows past N, chunks past K and x rows past M are buffer loads at an
+// out-of-range offset, which return zero without a memory access.  Waves
+// are added in LDS in wave order; the epilogue multiplies by s_g and rounds
+// to bf16 (RNE).
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace nvfp4 {
 
-namespace {
-constexpr int kRows = 16;       // weight rows per workgroup (one MFMA tile)
-constexpr int kWaves = 8;
-constexpr int kSegs = kWaves * 4;
-}  // namespace
-
-// Unpack 8 codes (one dword) times the block scale into 8 exact bf16 values.
-__device__ __forceinline__ bf16x8 unpack8_bf16(uint32_t c, float sb) {
+// 8 codes -> 8 exact bf16 values q * sb.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8_scaled(uint32_t c, float sb) {
   float q[8];
   fp4x8_to_f32(c, q);
   bf16x8 r;
@@ -37,94 +41,167 @@ __device__ __forceinline__ bf16x8 unpack8_bf16(uint32_t c, float sb) {
   return r;
 }
 
-// grid: ceil(N / 16) workgroups of 512 threads.  Segment length q (a
-// multiple of 32) covers K in kSegs segments; TMAX >= q / 32 chunks of 32
-// codes per lane are loaded at once (longer segments loop).
-// bf16_out: y bf16 [M, N]; otherwise fp32.
-template <int TMAX>
-__global__ __launch_bounds__(512) void gemv_w4a16_kernel(const uint16_t* __restrict__ x,
-                                                         const uint8_t* __restrict__ codes,
-                                                         const uint8_t* __restrict__ scales,
-                                                         const float* __restrict__ sg_ptr, int M, int N, int K,
-                                                         int q, int bf16_out, void* __restrict__ out) {
-  __shared__ f32x4 red[kWaves][64];
+// Sum of v over the 4 lane groups (lanes n, n+16, n+32, n+48): lane (n, g)
+// returns the total of component g.
+__device__ __forceinline__ float group_sum4(f32x4 v, int lane) {
+  const bool u32 = (lane & 32) != 0, u16 = (lane & 16) != 0;
+  float k0 = u32 ? v[2] : v[0], k1 = u32 ? v[3] : v[1];
+  float s0 = u32 ? v[0] : v[2], s1 = u32 ? v[1] : v[3];
+  k0 += __shfl_xor(s0, 32);
+  k1 += __shfl_xor(s1, 32);
+  float k = u16 ? k1 : k0, s = u16 ? k0 : k1;
+  return k + __shfl_xor(s, 16);
+}
+
+// Scale pairs of a pass.  Lane (n, g) loaded the 8 scale bytes of row n for
+// super-chunk s0 + g: halfword h = the two block scales of chunk 4 (s0 + g)
+// + h.  Returns in pair[u] the two scales of the lane's own chunk
+// 4 (s0 + u) + g, for u = 0..3 (a 4 x 4 transpose of halfwords between the
+// lanes n, n + 16, n + 32, n + 48).
+__device__ __forceinline__ void scale_pairs(u32x2 d, int lane, uint32_t pair[4]) {
+  const int g = lane >> 4;
+  const bool b1 = (g & 2) != 0, b0 = (g & 1) != 0;
+  const uint32_t keep = b1 ? d.y : d.x;  // halfwords b, b+1 (b = g & 2) of super-chunk s0 + g
+  const uint32_t recv = __shfl_xor(b1 ? d.x : d.y, 32);  // the same halfwords of super-chunk s0 + (g ^ 2)
+  const uint32_t send = b0 ? ((keep & 0xFFFFu) | (recv << 16)) : ((keep >> 16) | (recv & 0xFFFF0000u));
+  const uint32_t other = __shfl_xor(send, 16);  // halfword g of super-chunks s0 + (g ^ 1), s0 + (g ^ 3)
+  const uint32_t own = b0 ? (keep >> 16) : (keep & 0xFFFFu);
+  const uint32_t opp = b0 ? (recv >> 16) : (recv & 0xFFFFu);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int d2 = u ^ g;  // 0: own, 2: opp, 1: other.lo, 3: other.hi
+    pair[u] = d2 == 0 ? own : d2 == 2 ? opp : d2 == 1 ? (other & 0xFFFFu) : (other >> 16);
+  }
+}
+
+// grid: ceil(N / (16 T)) workgroups of NW waves.  DENSE: the M > 4 operand
+// layout; otherwise staggered (M <= 4).
+template <int DENSE, int T, int NW>
+__global__ __launch_bounds__(NW * 64) void gemv_w4a16_kernel(const uint16_t* __restrict__ x,
+                                                             const uint8_t* __restrict__ codes,
+                                                             const uint8_t* __restrict__ scales,
+                                                             const float* __restrict__ sg_ptr, int M, int N, int K,
+                                                             int bf16_out, void* __restrict__ out) {
+  constexpr int SW = 4;              // super-chunks per pass (one 8-byte scale load per lane)
+  constexpr int XL = DENSE ? 4 : 1;  // x loads per super-chunk
+  __shared__ f32x4 red[NW][T][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int nl = lane & 15;   // B column (weight row) / A row (x row)
-  const int h = lane >> 4;    // lane group
-  const int n0 = blockIdx.x * kRows;
-  const int row = min(n0 + nl, N - 1);
-  const int kseg = (4 * wave + h) * q;
-  const int kend = min(kseg + q, K);
-  const uint8_t* crow = codes + (int64_t)row * (K / 2);
-  const uint8_t* srow = scales + (int64_t)row * (K / 16);
-  const bool a_live = nl < M;
-  const uint16_t* xrow = x + (int64_t)(a_live ? nl : 0) * K;
+  const int nl = lane & 15, g = lane >> 4;
+  const int n0 = blockIdx.x * (16 * T);
+  const int rows = min(16 * T, N - n0);
+  const int half = K / 2, sbytes = K / 16;
+  const __amdgpu_buffer_rsrc_t cbuf = make_buf(codes + (int64_t)n0 * half, (uint32_t)(rows * half));
+  const __amdgpu_buffer_rsrc_t sbuf = make_buf(scales + (int64_t)n0 * sbytes, (uint32_t)(rows * sbytes));
+  const __amdgpu_buffer_rsrc_t xbuf = make_buf(x, (uint32_t)(M * K * 2));
+  const int nch = K / 32;
+  const int nsc = (nch + 3) / 4;
+  const int per = (nsc + NW - 1) / NW;
+  const int sbeg = wave * per, send = min(sbeg + per, nsc);
+  // x role: dense lane (m, g) holds row m; staggered lane (4 j + i, g) holds
+  // row i for MFMA j = jx.
+  const int xm = DENSE ? nl : (nl & 3);
+  const int jx = nl >> 2;
+  auto x_off = [&](int s) {
+    const int c = 4 * s + g;
+    return (xm < M && s < send && c < nch) ? (xm * K + 32 * c) * 2 + (DENSE ? 0 : 16 * jx) : kBufOOB;
+  };
 
-  // Every lane runs the same passes and MFMAs (an MFMA reads the operand
-  // registers of all 64 lanes); chunks outside a lane's segment are zero.
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int p0 = 0; p0 < q; p0 += 32 * TMAX) {
-    const int kp = kseg + p0;
-    // all weight loads of this pass first
-    u32x4 cw[TMAX];
-    uint32_t sw[TMAX];
+  f32x4 acc[T];
 #pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-      int k = kp + 32 * t;
-      int kk = k < kend ? k : 0;
-      cw[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(crow + kk / 2));
-      sw[t] = *reinterpret_cast<const uint16_t*>(srow + kk / 16);
+  for (int t = 0; t < T; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const bool wide_scales = (sbytes & 7) == 0;  // K % 128 == 0: 8-byte aligned scale windows inside each row
+  for (int s0 = sbeg; s0 < send; s0 += SW) {  // wave-uniform
+    // Issue order: x (L2 hits) for the whole pass, then scales, then codes,
+    // so the scale transpose and the first MFMAs wait only for what they use.
+    u32x4 xa[SW][XL];
+#pragma unroll
+    for (int u = 0; u < SW; ++u) {
+      const int off = x_off(s0 + u);
+#pragma unroll
+      for (int j = 0; j < XL; ++j) xa[u][j] = __builtin_amdgcn_raw_buffer_load_b128(xbuf, off + 16 * j, 0, 0);
     }
-    // x for the first chunk: unconditional loads from a clamped k.  A rows
-    // m >= M only reach output rows that are never stored, and chunks past a
-    // segment meet zero B operands, so these values need no masking.
-    u32x4 xa[2][4];
+    u32x2 sw[T];
     {
-      const int kc = kp < kend ? kp : 0;
+      // scale bytes [8 (s0 + g), 8 (s0 + g) + 8) of row n
+      const int sc = s0 + g;
+      const bool ok = sc < send && 4 * sc < nch;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) xa[0][j] = *reinterpret_cast<const u32x4*>(xrow + kc + 8 * j);
+      for (int t = 0; t < T; ++t) {
+        const int base = (16 * t + nl) * sbytes + 8 * sc;
+        if (wide_scales) {  // uniform
+          sw[t] = __builtin_amdgcn_raw_buffer_load_b64(sbuf, ok ? base : kBufOOB, 0, kBufNT);
+        } else {            // K % 128 != 0: one halfword per chunk, chunks past K read as zero
+          uint32_t h[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            h[q] = __builtin_amdgcn_raw_buffer_load_b16(sbuf, ok && 4 * sc + q < nch ? base + 2 * q : kBufOOB, 0,
+                                                        kBufNT);
+          sw[t] = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+        }
+      }
+    }
+    u32x4 cw[SW][T];
+#pragma unroll
+    for (int u = 0; u < SW; ++u) {
+      const int c = 4 * (s0 + u) + g;
+      const bool ok = s0 + u < send && c < nch;
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+        cw[u][t] = __builtin_amdgcn_raw_buffer_load_b128(cbuf, ok ? (16 * t + nl) * half + 16 * c : kBufOOB, 0, kBufNT);
     }
     __builtin_amdgcn_sched_barrier(0);
+    uint32_t pairs[T][4];
 #pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-      const int k = kp + 32 * t;
-      const bool live = k < kend;
-      const int cur = t & 1;
-      if (t + 1 < TMAX) {
-        const int k1 = k + 32;
-        const int kc = k1 < kend ? k1 : 0;
+    for (int t = 0; t < T; ++t) scale_pairs(sw[t], lane, pairs[t]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xa[cur ^ 1][j] = *reinterpret_cast<const u32x4*>(xrow + kc + 8 * j);
-      }
-      const float sb0 = e4m3_to_f32(sw[t] & 0xFFu), sb1 = e4m3_to_f32(sw[t] >> 8);
+    for (int u = 0; u < SW; ++u) {
+      if (s0 + u < send) {  // wave-uniform
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bf16x8 b = live ? unpack8_bf16(cw[t][j], j < 2 ? sb0 : sb1) : bf16x8{};
-        bf16x8 a = __builtin_bit_cast(bf16x8, xa[cur][j]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+        for (int t = 0; t < T; ++t) {
+          const f32x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(pairs[t][u], 1.0f, false);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const u32x4 z4 = {0u, 0u, 0u, 0u};
+            const u32x4 a = DENSE ? xa[u][DENSE ? j : 0] : (jx == j ? xa[u][0] : z4);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                             fp4x8_to_bf16x8_scaled(cw[u][t][j], j < 2 ? sc.x : sc.y),
+                                                             acc[t], 0, 0, 0);
+          }
+        }
       }
     }
   }
 
-  // acc[i] = partial C[m = 4h + i][n = nl]; add the 8 waves in order.
-  red[wave][lane] = acc;
+  // dense: lane (n, g) holds rows m = 4 g + i.  staggered: lane (n, g) holds
+  // rows 4 g + i = x row i times the codes of MFMA g; the sum over the lane
+  // groups leaves row m = g in lane (n, g).
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    if (DENSE) {
+      red[wave][t][lane] = acc[t];
+    } else {
+      const float v = group_sum4(acc[t], lane);
+      red[wave][t][lane] = f32x4{v, 0.f, 0.f, 0.f};
+    }
+  }
   __syncthreads();
-  if (wave == 0) {
-    f32x4 s = red[0][lane];
+  const float sg = *sg_ptr;
+  for (int idx = threadIdx.x; idx < T * 64; idx += NW * 64) {
+    const int t = idx >> 6, l = idx & 63;
+    f32x4 sum = red[0][t][l];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) s += red[w][lane];
-    const float sg = *sg_ptr;
-    const int n = n0 + nl;
-    if (n < N) {
+    for (int w = 1; w < NW; ++w) sum += red[w][t][l];
+    const int n = n0 + 16 * t + (l & 15);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 4 * h + i;
-        if (m >= M) continue;
+    for (int i = 0; i < (DENSE ? 4 : 1); ++i) {
+      const int m = DENSE ? 4 * (l >> 4) + i : (l >> 4);
+      if (m < M && n < N) {
         if (bf16_out)
-          reinterpret_cast<uint16_t*>(out)[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_bits(s[i] * sg);
+          reinterpret_cast<uint16_t*>(out)[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_bits(sum[i] * sg);
         else
-          reinterpret_cast<float*>(out)[(int64_t)m * N + n] = s[i] * sg;
+          reinterpret_cast<float*>(out)[(int64_t)m * N + n] = sum[i] * sg;
       }
     }
   }
@@ -286,18 +363,24 @@ hipError_t launch_gemv_w4a16(const uint16_t* x, const uint8_t* codes, const uint
 #undef NVFP4_GEMV_M1
     return hipGetLastError();
   }
-  int64_t q = ((K + kSegs - 1) / kSegs + 31) / 32 * 32;   // segment length, a multiple of 32
-  int64_t chunks = q / 32;
-  dim3 grid((unsigned)((N + kRows - 1) / kRows));
-  if (chunks <= 4)
-    hipLaunchKernelGGL(gemv_w4a16_kernel<4>, grid, dim3(512), 0, stream, x, codes, scales, sg, (int)M, (int)N,
-                       (int)K, (int)q, b, y);
-  else if (chunks <= 8)
-    hipLaunchKernelGGL(gemv_w4a16_kernel<8>, grid, dim3(512), 0, stream, x, codes, scales, sg, (int)M, (int)N,
-                       (int)K, (int)q, b, y);
-  else
-    hipLaunchKernelGGL(gemv_w4a16_kernel<16>, grid, dim3(512), 0, stream, x, codes, scales, sg, (int)M, (int)N,
-                       (int)K, (int)q, b, y);
+  // M > 1: MFMA kernels.  32 rows per workgroup when that still gives at
+  // least one workgroup per CU (256), else 16; 16 waves split long rows.
+  const int dense = M > 4 ? 1 : 0;
+  const bool t2 = N >= 32 * 256;
+  const bool nw16 = !t2 && K >= 8192;
+#define NVFP4_GEMV_MFMA(D, T, NW)                                                                                 \
+  hipLaunchKernelGGL((gemv_w4a16_kernel<D, T, NW>), dim3((unsigned)((N + 16 * T - 1) / (16 * T))), dim3(NW * 64), \
+                     0, stream, x, codes, scales, sg, (int)M, (int)N, (int)K, b, y)
+  if (dense) {
+    if (t2) NVFP4_GEMV_MFMA(1, 2, 8);
+    else if (nw16) NVFP4_GEMV_MFMA(1, 1, 16);
+    else NVFP4_GEMV_MFMA(1, 1, 8);
+  } else {
+    if (t2) NVFP4_GEMV_MFMA(0, 2, 8);
+    else if (nw16) NVFP4_GEMV_MFMA(0, 1, 16);
+    else NVFP4_GEMV_MFMA(0, 1, 8);
+  }
+#undef NVFP4_GEMV_MFMA
   return hipGetLastError();
 }
 

@@ -132,7 +132,7 @@ int nvfp4_gemv_w4a16(const void* x, const uint8_t* w_codes, const uint8_t* w_sca
   if (y_dtype != NVFP4_F32 && y_dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
   if (M < 0 || N < 0 || K < 0 || !mul_ok(M, K) || !mul_ok(N, K) || !mul_ok(M, N)) return NVFP4_ERR_SHAPE;
   if (K % 16 != 0) return NVFP4_ERR_SHAPE;
-  if (K % 32 != 0 || M > 16 || K > (int64_t)1 << 30 || N > (int64_t)1 << 30) return NVFP4_ERR_UNSUPPORTED;
+  if (K % 32 != 0 || M > 16 || K > (int64_t)1 << 24 || N > (int64_t)1 << 30) return NVFP4_ERR_UNSUPPORTED;
   if (!aligned(x, 16) || !aligned(w_codes, 16) || !aligned(w_scales, 4) || !aligned(w_global, 4) ||
       !aligned(y, 4))
     return NVFP4_ERR_ALIGN;

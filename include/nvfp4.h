@@ -133,8 +133,9 @@ int nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const float* glob
  *   workspace reserved: this version needs none
  *            (nvfp4_workspace_bytes(NVFP4_OP_GEMV_W4A16, M, N) returns 0);
  *            may be NULL
- *   0 <= M <= 16 (the decode batch; M = 0 or N = 0 is a no-op); fp32
- *   accumulation, fp32 epilogue (x s_gW), round-to-nearest-even bf16 output.
+ *   0 <= M <= 16 (the decode batch; M = 0 or N = 0 is a no-op); K % 32 == 0
+ *   and 0 < K <= 2^24, otherwise NVFP4_ERR_UNSUPPORTED.  fp32 accumulation,
+ *   fp32 epilogue (x s_gW), round-to-nearest-even bf16 output.
  */
 int nvfp4_gemv_w4a16(const void* x, const uint8_t* w_codes, const uint8_t* w_scales,
                      const float* w_global, int64_t M, int64_t N, int64_t K,

@@ -86,6 +86,7 @@ def test_gemv_validation():
     assert f(A16, A16, A16, A4, 17, 64, 64, A16, nv.BF16, None, 0, None) == nv.ERR_UNSUPPORTED
     assert f(A16, A16, A16, A4, 1, 64, 48, A16, nv.BF16, None, 0, None) == nv.ERR_UNSUPPORTED
     assert f(A16 + 2, A16, A16, A4, 1, 64, 64, A16, nv.BF16, None, 0, None) == nv.ERR_ALIGN
+    assert f(A16, A16, A16, A4, 1, 64, (1 << 24) + 32, A16, nv.BF16, None, 0, None) == nv.ERR_UNSUPPORTED
     assert f(A16, A16, A16, A4, 0, 64, 64, A16, nv.BF16, None, 0, None) == nv.OK      # empty: no launch
 
 

@@ -33,8 +33,8 @@ def test_tiny_config_gemv():
     assert_within_tau(y32.reshape(-1), ystar, tau, "tiny fp32")
 
 
-@pytest.mark.parametrize("shape", [(64, 32), (100, 160), (1000, 1056), (33, 4096)])
-@pytest.mark.parametrize("M", [1, 3, 16])
+@pytest.mark.parametrize("shape", [(64, 32), (100, 160), (300, 96), (1000, 1056), (33, 4096)])
+@pytest.mark.parametrize("M", [1, 3, 4, 5, 8, 16])
 def test_gemv_ragged(shape, M):
     N, K = shape
     print(f"[case] gemv N={N} K={K} M={M}", flush=True)
