@@ -33,6 +33,13 @@ def build(verbose: bool = False, extra=()) -> str:
         raise RuntimeError("hipcc failed:\n" + err)
     if verbose and err:
         print(err)
+    # -shared links with unresolved symbols allowed; a kernel whose host stub
+    # failed to instantiate would only show up at load time.  Refuse it here.
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in nm.stdout.splitlines() if "nvfp4" in l]
+    if nm.returncode != 0 or missing:
+        os.remove(tmp)
+        raise RuntimeError("libnvfp4.so has unresolved library symbols: " + ", ".join(missing or [nm.stderr]))
     os.replace(tmp, OUT)
     return OUT
 

@@ -103,25 +103,58 @@ __device__ __forceinline__ f16x2 e4m3x2_to_f16x2(uint32_t b) {
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false);
 }
 
+// s_waitcnt immediate: at most n vector memory operations outstanding, all
+// LDS operations complete (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt
+// 6:4 = 7 means no wait, lgkmcnt 11:8).
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+
+// 16 (2) bytes per lane from a buffer straight into LDS: lane i of the wave
+// writes 16 bytes at lds_base + 16 i (the 2 bytes zero-extended to the dword
+// at lds_base + 4 i); offsets past the buffer write zeros.
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t buf, u32x4* lds_base, uint32_t voff,
+                                                uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(buf, (__attribute__((address_space(3))) void*)lds_base, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void buffer_to_lds2(__amdgpu_buffer_rsrc_t buf, uint32_t* lds_base, uint32_t voff,
+                                               uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(buf, (__attribute__((address_space(3))) void*)lds_base, 2, voff, soff, 0, 0);
+}
+
 // BM x BN tile per workgroup of WM x WN waves; each wave (BM/WM) x (BN/WN)
 // as TM x TN tiles of 32x32.  grid.x enumerates tiles (XCD-aware order).
-// K loop: A tiles are double buffered in LDS and fetched two K steps ahead
-// into one of two register sets; packed weights are fetched two K steps
-// ahead into registers.  The loop is unrolled by two so every register set
-// is addressed statically.
+// K loop, one step per 64 k.  Every operand goes global -> LDS directly
+// (buffer loads with the LDS bit; rows past M or N read as zero) into three
+// stages fetched two steps ahead, so no register holds data in flight:
+//  * A^ (fp16): a lane's DMA target is fixed by its lane number, so each
+//    lane fetches the 16-byte chunk that belongs in its LDS slot under an
+//    XOR swizzle (conflict-free 16-byte fragment reads).
+//  * packed weights: row r's 32 code bytes of the step sit in two 16-byte
+//    slots, swapped for rows with bit 2 set (conflict-free reads); the 4
+//    scale bytes of a row are contiguous.
+// One barrier per step, after an explicit wait for this step's stage.  Each
+// lane reads its weight chunk and scales once per step and unpacks 8 codes
+// per MFMA sub-step (hardware FP4 -> fp16 converter, one packed multiply by
+// the block scale); A fragments are read one sub-step ahead of their MFMAs.
+// The loop is unrolled by 3 so the stages (separate LDS arrays) are
+// addressed statically.
 template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2))) void gemm_w4a4_kernel(const uint16_t* __restrict__ a_hat,
-                                                                 const float* __restrict__ sga_ptr,
-                                                                 const uint8_t* __restrict__ codes,
-                                                                 const uint8_t* __restrict__ scales,
-                                                                 const float* __restrict__ sgw_ptr, int M, int N,
-                                                                 int K, void* __restrict__ y, int bf16_out) {
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2))) void gemm_w4a4_kernel(
+    const uint16_t* __restrict__ a_hat, const float* __restrict__ sga_ptr, const uint8_t* __restrict__ codes,
+    const uint8_t* __restrict__ scales, const float* __restrict__ sgw_ptr, int M, int N, int K, void* __restrict__ y,
+    int bf16_out) {
   constexpr int NT = WM * WN * 64;                       // threads
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;    // 32x32 tiles per wave
-  constexpr int A_CHUNKS = BM * BK * 2 / 16;             // 16-byte chunks per A tile
-  constexpr int APT = A_CHUNKS / NT;
-  static_assert(A_CHUNKS % NT == 0, "A tile must split evenly over the threads");
-  __shared__ __attribute__((aligned(16))) u32x4 lds_a[2][A_CHUNKS];
+  constexpr int A_CHUNKS = BM * BK * 2 / 16;             // 16-byte chunks per A stage
+  constexpr int APT = A_CHUNKS / NT;                     // A DMA instructions per lane and step
+  constexpr int W_CHUNKS = BN * 2;                       // 16-byte code chunks per W stage
+  static_assert(A_CHUNKS % NT == 0 && W_CHUNKS == NT && BN * 2 == NT, "tile shape must match the thread count");
+  constexpr int VM_STEP = APT + 2;                       // vector memory instructions per lane and step
+  struct Stage {
+    u32x4 a[A_CHUNKS];
+    u32x4 w[W_CHUNKS];
+    uint32_t s[BN * 2];
+  };
+  __shared__ __attribute__((aligned(16))) Stage st0, st1, st2;
 
   // Tile coordinates.  Consecutive workgroup ids go to different XCDs
   // (round robin over 8); remap so each XCD receives a contiguous run of
@@ -146,23 +179,34 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int l32 = lane & 31, g = lane >> 5;  // MFMA row/col and k lane group
+  const int KT = K / BK;
 
-  // ---- A global -> LDS mapping: chunk tid + NT j -> row tid / 8 + j NT / 8,
-  // 16-byte chunk tid % 8 of the row's 64 k; LDS slot XOR-swizzled by row.
-  // NT / 8 is a multiple of 8, so every row of a thread has the same swizzle.
-  const int a_r0 = tid >> 3, a_c = tid & 7;
-  const int a_slot0 = a_r0 * 8 + (a_c ^ (a_r0 & 7));
-  const u32x4* a_base = reinterpret_cast<const u32x4*>(a_hat) + a_c;
-
-  // ---- W rows of this lane: TN sub-tiles, row n0 + wn*(BN/WN) + 32 t + l32
-  const uint8_t* wc[TN];
-  const uint8_t* wsc[TN];
+  // ---- DMA sources.  A: instruction j of wave w fills slots
+  // [64 (w APT + j), +64); slot S holds row S / 8, 16-byte chunk
+  // (S % 8) ^ (row % 8) of the step's 64 k.
+  const __amdgpu_buffer_rsrc_t abuf = make_buf(a_hat + (int64_t)m0 * K, (uint32_t)(min(BM, M - m0) * K * 2));
+  uint32_t a_off[APT];
 #pragma unroll
-  for (int t = 0; t < TN; ++t) {
-    int n = min(n0 + wn * (BN / WN) + 32 * t + l32, N - 1);
-    wc[t] = codes + (int64_t)n * (K / 2) + 16 * g;      // 32 codes = 16 bytes per K step
-    wsc[t] = scales + (int64_t)n * (K / 16) + 2 * g;    // 2 scale bytes per K step
+  for (int j = 0; j < APT; ++j) {
+    const int S = 64 * (wave * APT + j) + lane;
+    const int r = S >> 3, c = (S & 7) ^ (r & 7);
+    a_off[j] = (uint32_t)((r * K + 8 * c) * 2);
   }
+  // W codes: thread t fills slot t = row t / 2, half (t % 2) ^ ((row >> 2) & 1).
+  // Scales: thread t fills dword slot t with bytes 2 (t % 2) .. +2 of row t / 2.
+  const int w_rows = min(BN, N - n0);
+  const __amdgpu_buffer_rsrc_t wbuf = make_buf(codes + (int64_t)n0 * (K / 2), (uint32_t)(w_rows * (K / 2)));
+  const __amdgpu_buffer_rsrc_t sbuf = make_buf(scales + (int64_t)n0 * (K / 16), (uint32_t)(w_rows * (K / 16)));
+  const uint32_t w_off = (uint32_t)((tid >> 1) * (K / 2) + 16 * ((tid & 1) ^ ((tid >> 3) & 1)));
+  const uint32_t s_off = (uint32_t)((tid >> 1) * (K / 16) + 2 * (tid & 1));
+
+  auto dma = [&](Stage& stg, int kt) {
+    const uint32_t k = (uint32_t)min(kt, KT - 1);
+#pragma unroll
+    for (int j = 0; j < APT; ++j) buffer_to_lds16(abuf, stg.a + 64 * (wave * APT + j), a_off[j], k * (BK * 2));
+    buffer_to_lds16(wbuf, stg.w + 64 * wave, w_off, k * (BK / 2));
+    buffer_to_lds2(sbuf, stg.s + 64 * wave, s_off, k * (BK / 16));
+  };
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -172,98 +216,97 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][t][r] = 0.0f;
 
-  const int KT = K / BK;
-  u32x4 aset0[APT], aset1[APT];
-  u32x4 wset0[TN], wset1[TN];
-  uint32_t sset0[TN], sset1[TN];
-  auto load_a = [&](u32x4 (&dst)[APT], int kt) {
-    const int kk = min(kt, KT - 1) * (BK / 8);
+  // A fragment of sub-step s for tile row i: row r = wm*(BM/WM) + 32 i + l32
+  // (r % 8 == l32 % 8), chunk 4 g + s.  W chunk of tile column t: row
+  // rw = wn*(BN/WN) + 32 t + l32, half g; scale bytes 2 g, 2 g + 1 of the row.
+  int a_row8[TM];
 #pragma unroll
-    for (int j = 0; j < APT; ++j) {
-      const int row = min(m0 + a_r0 + j * (NT / 8), M - 1);
-      dst[j] = a_base[(int64_t)row * (K / 8) + kk];
-    }
-  };
-  auto load_w = [&](u32x4 (&dw)[TN], uint32_t (&ds)[TN], int kt) {
-    const int kk = min(kt, KT - 1);
+  for (int i = 0; i < TM; ++i) a_row8[i] = (wm * (BM / WM) + 32 * i + l32) * 8;
+  const int a_sw = l32 & 7;
+  int w_slot[TN], s_slot[TN];
 #pragma unroll
-    for (int t = 0; t < TN; ++t) {
-      dw[t] = *reinterpret_cast<const u32x4*>(wc[t] + kk * (BK / 2));
-      ds[t] = *reinterpret_cast<const uint16_t*>(wsc[t] + kk * (BK / 16));
-    }
-  };
-  auto store_a = [&](const u32x4 (&src)[APT], int buf) {
-#pragma unroll
-    for (int j = 0; j < APT; ++j) lds_a[buf][a_slot0 + j * NT] = src[j];
-  };
-  // one K step of 64 = 4 sub-steps of 16 from LDS buffer `buf`
-  auto compute = [&](int buf, const u32x4 (&wr)[TN], const uint32_t (&sr)[TN]) {
+  for (int t = 0; t < TN; ++t) {
+    const int rw = wn * (BN / WN) + 32 * t + l32;
+    w_slot[t] = 2 * rw + (g ^ ((rw >> 2) & 1));
+    s_slot[t] = 2 * rw + g;
+  }
+
+  // one K step of 64 = 4 sub-steps of 16 from a stage.  Software pipeline:
+  // the A fragments and unpacked weights of sub-step s+1 are produced while
+  // the MFMAs of sub-step s run (sched_group_barrier pins the interleave:
+  // each MFMA is followed by one LDS read and four VALU operations).
+  auto compute = [&](const Stage& stg) {
+    u32x4 wr[TN];
     f16x2 sc0[TN], sc1[TN];
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
-      f16x2 s2 = e4m3x2_to_f16x2(sr[t]);
+      wr[t] = stg.w[w_slot[t]];
+      f16x2 s2 = e4m3x2_to_f16x2(stg.s[s_slot[t]]);
       sc0[t] = f16x2{s2.x, s2.x};
       sc1[t] = f16x2{s2.y, s2.y};
     }
+    f16x8 af[2][TM], bf[2][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[0][i] = __builtin_bit_cast(f16x8, stg.a[a_row8[i] + ((4 * g) ^ a_sw)]);
+#pragma unroll
+    for (int t = 0; t < TN; ++t) bf[0][t] = unpack8_f16(wr[t][0], sc0[t]);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      f16x8 afrag[TM];
+      const int cb = s & 1, nb = cb ^ 1;
+      if (s < 3) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        int r = wm * (BM / WM) + 32 * i + l32;
-        afrag[i] = __builtin_bit_cast(f16x8, lds_a[buf][r * 8 + ((4 * g + s) ^ (r & 7))]);
+        for (int i = 0; i < TM; ++i)
+          af[nb][i] = __builtin_bit_cast(f16x8, stg.a[a_row8[i] + ((4 * g + s + 1) ^ a_sw)]);
+#pragma unroll
+        for (int t = 0; t < TN; ++t) bf[nb][t] = unpack8_f16(wr[t][s + 1], s + 1 < 2 ? sc0[t] : sc1[t]);
       }
-      f16x8 bfrag[TN];
-#pragma unroll
-      for (int t = 0; t < TN; ++t) bfrag[t] = unpack8_f16(wr[t][s], s < 2 ? sc0[t] : sc1[t]);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int t = 0; t < TN; ++t)
-          acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afrag[i], bfrag[t], acc[i][t], 0, 0, 0);
+          acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cb][i], bf[cb][t], acc[i][t], 0, 0, 0);
     }
+    // schedule: operand reads and sub-step 0 unpack, then per sub-step the
+    // MFMAs interleaved with the next sub-step's reads and unpack
+    constexpr int kMFMA = 0x008, kVALU = 0x002, kDSR = 0x100;
+    __builtin_amdgcn_sched_group_barrier(kDSR, 2 * TN + TM, 0);
+    __builtin_amdgcn_sched_group_barrier(kVALU, 8 * TN + 4, 0);
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+#pragma unroll
+      for (int q = 0; q < TM * TN; ++q) {
+        __builtin_amdgcn_sched_group_barrier(kMFMA, 1, 0);
+        if (q < TM) __builtin_amdgcn_sched_group_barrier(kDSR, 1, 0);
+        if (q < 4) __builtin_amdgcn_sched_group_barrier(kVALU, 2 * TN, 0);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(kMFMA, TM * TN, 0);
   };
 
-  // prologue: A(0) -> LDS buffer 0; A(1) in flight in aset0; W(0), W(1) in flight
-  load_a(aset1, 0);
-  load_w(wset0, sset0, 0);
-  load_w(wset1, sset1, 1);
-  store_a(aset1, 0);
-  load_a(aset0, 1);
-  for (int kt = 0; kt < KT; kt += 2) {
-    {  // even step: LDS 0 holds A(kt); aset0 = A(kt+1); wset0 = W(kt)
-      __syncthreads();
-      u32x4 wcur[TN];
-      uint32_t scur[TN];
-#pragma unroll
-      for (int t = 0; t < TN; ++t) {
-        wcur[t] = wset0[t];
-        scur[t] = sset0[t];
-      }
-      load_a(aset1, kt + 2);
-      load_w(wset0, sset0, kt + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(0, wcur, scur);
-      __builtin_amdgcn_sched_barrier(0);
-      store_a(aset0, 1);
-    }
-    if (kt + 1 < KT) {  // odd step: LDS 1 holds A(kt+1); aset1 = A(kt+2); wset1 = W(kt+1)
-      __syncthreads();
-      u32x4 wcur[TN];
-      uint32_t scur[TN];
-#pragma unroll
-      for (int t = 0; t < TN; ++t) {
-        wcur[t] = wset1[t];
-        scur[t] = sset1[t];
-      }
-      load_a(aset0, kt + 3);
-      load_w(wset1, sset1, kt + 3);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(1, wcur, scur);
-      __builtin_amdgcn_sched_barrier(0);
-      store_a(aset1, 0);
-    }
+  // Step kt: operands of kt in stage `cur`; stage `nxt2` (read last in step
+  // kt-1) receives kt+2.  After the DMA of kt this lane issued those of kt+1.
+  auto step = [&](int kt, const Stage& cur, Stage& nxt2) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(VM_STEP));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    dma(nxt2, kt + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cur);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  dma(st0, 0);
+  dma(st1, 1);
+  int kt = 0;
+  for (; kt + 3 <= KT; kt += 3) {
+    step(kt + 0, st0, st2);
+    step(kt + 1, st1, st0);
+    step(kt + 2, st2, st1);
   }
+  if (kt + 0 < KT) step(kt + 0, st0, st2);
+  if (kt + 1 < KT) step(kt + 1, st1, st0);
+  // Drain the DMA still in flight into LDS before the workgroup exits.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
 
   // ---- epilogue: acc[i][t][r] = C[row = 8 (r/4) + 4 g + r%4][col = l32]
   const float alpha = (*sga_ptr) * (*sgw_ptr);
