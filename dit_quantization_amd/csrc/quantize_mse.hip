@@ -15,33 +15,29 @@
 // order, replaced only on a strictly smaller error.
 //
 // Design: the search is ALU work, so one lane owns one 16-element block and
-// walks its ~16 candidates with no cross-lane traffic.  Element codes per
-// candidate come from the hardware E2M1 converter applied to x (1 -+ 2^-17)
-// for the approximate fp32 quotient x: when both ends round to the same
-// value, so does the exact quotient (the fp32 error is below 2^-21
-// relative); otherwise the exact fp64 comparison decides.
+// walks its ~16 candidates with no cross-lane traffic.  Each lane iterates
+// over its own candidate list (the wave runs as many iterations as its
+// longest list, not the union of the lanes' code ranges).  Element codes per
+// candidate come from the hardware E2M1 converter applied to the fp32
+// quotient x = |W| (1 / c) (1 / s_g), whose relative error is below 3 ulps.
+// Every E2M1 rounding midpoint has at most 3 significant bits, so when no
+// x of the block lies within 8 ulps of a number whose low 21 mantissa bits
+// are zero, x and the exact quotient round alike and the fast codes stand;
+// otherwise (rare) the block's codes for that candidate come from exact fp64
+// comparisons.  The error terms are computed in fp64 exactly as specified.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace nvfp4 {
 
 namespace {
-constexpr float kLo = 1.0f - 0x1p-17f;
-constexpr float kHi = 1.0f + 0x1p-17f;
+// ((bits(x) + 8) << 11) < (16 << 11)  <=>  the low 21 mantissa bits of x
+// are within -8..+7 of zero (mod 2^21).  Zero inputs get bit 20 added so
+// that they never test positive.
+constexpr uint32_t kNearOff = 8u << 11;
+constexpr uint32_t kZeroOff = (0x00100000u + 8u) << 11;
+constexpr uint32_t kNearLim = 16u << 11;
 }  // namespace
-
-// fp32 magnitude of the E2M1 value nearest to aw / (c s_g), aw >= 0.
-__device__ __forceinline__ float e2m1_mag(float aw, float inv, bool fast, double cs) {
-  float x = aw * inv;
-  uint32_t byte = NVFP4_CVT_PK_FP4(0u, x * kLo, x * kHi, 0);
-  f32x2 q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(byte, 1.0f, 0);
-  if (!fast || q.x != q.y) {
-    uint32_t c = e2m1_code_exact(aw, cs);
-    f32x2 e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
-    return e.x;
-  }
-  return q.x;
-}
 
 template <bool kBF16>
 __device__ __forceinline__ void load16(const void* __restrict__ x, int64_t b, float w[16]) {
@@ -87,7 +83,7 @@ __global__ __launch_bounds__(256) void quantize_mse_kernel(const void* __restric
     }
     const double m = (double)mf;
     const double a = m / six_sg;
-    const uint32_t kabs = e4m3_code_rne(a);
+    const int kabs = (int)e4m3_code_rne(a);
     // Window [k_lo, k_hi] of codes c >= 1 with a/2 <= c <= 2a (exact tests).
     int klo = (int)e4m3_code_rne(a * 0.5);
     if (klo < 1) klo = 1;
@@ -96,31 +92,60 @@ __global__ __launch_bounds__(256) void quantize_mse_kernel(const void* __restric
     int khi = (int)e4m3_code_rne(a * 2.0);
     if (khi >= 1 && 3.0 * sg64 * (double)e4m3_to_f32(khi) > m) --khi;
     if (khi < (int)kE4M3MaxCode && 3.0 * sg64 * (double)e4m3_to_f32(khi + 1) <= m) ++khi;
-    const int kfirst = min(klo, (int)kabs), klast = max(khi, (int)kabs);
+    const int kfirst = min(klo, kabs), ncand = max(khi, kabs) - kfirst + 1;
+
+    double aw64[16];
+    uint32_t zoff[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      aw64[e] = (double)aw[e];
+      zoff[e] = aw[e] == 0.0f ? kZeroOff : kNearOff;
+    }
 
     double best_err = 0.0;
     int best = -1;
-    for (int k = kfirst; k <= klast; ++k) {
-      if ((k < klo || k > khi) && k != (int)kabs) continue;
+    for (int i = 0; i < ncand; ++i) {
+      const int k = kfirst + i;
+      if ((k < klo || k > khi) && k != kabs) continue;
       double err = 0.0;
       if (k == 0) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          double d = (double)aw[e];
-          err = err + d * d;
-        }
+        for (int e = 0; e < 16; ++e) err = err + aw64[e] * aw64[e];
       } else {
         const float c = e4m3_to_f32((uint32_t)k);
         const double cs = (double)c * sg64;  // exact
         const float inv = __builtin_amdgcn_rcpf(c) * inv_sg;
+        float q[16];
+        uint32_t tmin = 0xFFFFFFFFu;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float xs[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            xs[e] = aw[8 * h + e] * inv;
+            tmin = min(tmin, (__float_as_uint(xs[e]) << 11) + zoff[8 * h + e]);
+          }
+          uint32_t word = 0;
+          word = NVFP4_CVT_PK_FP4(word, xs[0], xs[1], 0);
+          word = NVFP4_CVT_PK_FP4(word, xs[2], xs[3], 1);
+          word = NVFP4_CVT_PK_FP4(word, xs[4], xs[5], 2);
+          word = NVFP4_CVT_PK_FP4(word, xs[6], xs[7], 3);
+          fp4x8_to_f32(word, q + 8 * h);
+        }
         const bool fast = inv < 0x1p100f && inv > 0x1p-100f;
+        if (!fast || tmin < kNearLim) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const f32x2 ex = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(e2m1_code_exact(aw[e], cs), 1.0f, 0);
+            q[e] = ex.x;
+          }
+        }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          float q = e2m1_mag(aw[e], inv, fast, cs);
           // |W| - c s_g |q|: c s_g q is exact, so the fused form rounds once,
           // like the separate subtraction of the exact product.
-          double d = __builtin_fma(-cs, (double)q, (double)aw[e]);
-          double sq = d * d;
+          const double d = __builtin_fma(-cs, (double)q[e], aw64[e]);
+          const double sq = d * d;
           err = err + sq;
         }
       }
