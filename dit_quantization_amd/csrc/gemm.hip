@@ -138,7 +138,7 @@ __device__ __forceinline__ void buffer_to_lds2(__amdgpu_buffer_rsrc_t buf, uint3
 // The loop is unrolled by 3 so the stages (separate LDS arrays) are
 // addressed statically.
 template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2))) void gemm_w4a4_kernel(
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu((BM / WM) * (BN / WN) >= 128 * 128 ? 1 : 2))) void gemm_w4a4_kernel(
     const uint16_t* __restrict__ a_hat, const float* __restrict__ sga_ptr, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ sgw_ptr, int M, int N, int K, void* __restrict__ y,
     int bf16_out) {
@@ -146,9 +146,10 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;    // 32x32 tiles per wave
   constexpr int A_CHUNKS = BM * BK * 2 / 16;             // 16-byte chunks per A stage
   constexpr int APT = A_CHUNKS / NT;                     // A DMA instructions per lane and step
-  constexpr int W_CHUNKS = BN * 2;                       // 16-byte code chunks per W stage
-  static_assert(A_CHUNKS % NT == 0 && W_CHUNKS == NT && BN * 2 == NT, "tile shape must match the thread count");
-  constexpr int VM_STEP = APT + 2;                       // vector memory instructions per lane and step
+  constexpr int W_CHUNKS = BN * 2;                       // 16-byte code chunks (and scale dwords) per W stage
+  constexpr int WPT = W_CHUNKS / NT;                     // W DMA instructions per lane and step (each kind)
+  static_assert(A_CHUNKS % NT == 0 && W_CHUNKS % NT == 0, "tile shape must match the thread count");
+  constexpr int VM_STEP = APT + 2 * WPT;                 // vector memory instructions per lane and step
   struct Stage {
     u32x4 a[A_CHUNKS];
     u32x4 w[W_CHUNKS];
@@ -192,20 +193,28 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
     const int r = S >> 3, c = (S & 7) ^ (r & 7);
     a_off[j] = (uint32_t)((r * K + 8 * c) * 2);
   }
-  // W codes: thread t fills slot t = row t / 2, half (t % 2) ^ ((row >> 2) & 1).
-  // Scales: thread t fills dword slot t with bytes 2 (t % 2) .. +2 of row t / 2.
+  // W codes: slot u (= tid + NT j) holds row u / 2, half (u % 2) ^ ((row >> 2) & 1).
+  // Scales: dword slot u holds bytes 2 (u % 2) .. +2 of row u / 2.
   const int w_rows = min(BN, N - n0);
   const __amdgpu_buffer_rsrc_t wbuf = make_buf(codes + (int64_t)n0 * (K / 2), (uint32_t)(w_rows * (K / 2)));
   const __amdgpu_buffer_rsrc_t sbuf = make_buf(scales + (int64_t)n0 * (K / 16), (uint32_t)(w_rows * (K / 16)));
-  const uint32_t w_off = (uint32_t)((tid >> 1) * (K / 2) + 16 * ((tid & 1) ^ ((tid >> 3) & 1)));
-  const uint32_t s_off = (uint32_t)((tid >> 1) * (K / 16) + 2 * (tid & 1));
+  uint32_t w_off[WPT], s_off[WPT];
+#pragma unroll
+  for (int j = 0; j < WPT; ++j) {
+    const int u = tid + NT * j;
+    w_off[j] = (uint32_t)((u >> 1) * (K / 2) + 16 * ((u & 1) ^ ((u >> 3) & 1)));
+    s_off[j] = (uint32_t)((u >> 1) * (K / 16) + 2 * (u & 1));
+  }
 
   auto dma = [&](Stage& stg, int kt) {
     const uint32_t k = (uint32_t)min(kt, KT - 1);
 #pragma unroll
     for (int j = 0; j < APT; ++j) buffer_to_lds16(abuf, stg.a + 64 * (wave * APT + j), a_off[j], k * (BK * 2));
-    buffer_to_lds16(wbuf, stg.w + 64 * wave, w_off, k * (BK / 2));
-    buffer_to_lds2(sbuf, stg.s + 64 * wave, s_off, k * (BK / 16));
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+      buffer_to_lds16(wbuf, stg.w + NT * j + 64 * wave, w_off[j], k * (BK / 2));
+      buffer_to_lds2(sbuf, stg.s + NT * j + 64 * wave, s_off[j], k * (BK / 16));
+    }
   };
 
   f32x16 acc[TM][TN];
@@ -231,13 +240,16 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
     s_slot[t] = 2 * rw + g;
   }
 
-  // one K step of 64 = 4 sub-steps of 16 from a stage.  Software pipeline:
-  // the A fragments and unpacked weights of sub-step s+1 are produced while
-  // the MFMAs of sub-step s run (sched_group_barrier pins the interleave:
-  // each MFMA is followed by one LDS read and four VALU operations).
-  auto compute = [&](const Stage& stg) {
-    u32x4 wr[TN];
-    f16x2 sc0[TN], sc1[TN];
+  // Operands of one K step (64 = 4 sub-steps of 16): each lane's weight
+  // chunk and scales, A fragments and unpacked weights of the current and
+  // next sub-step (software pipeline, double buffered).
+  u32x4 wr[TN];
+  f16x2 sc0[TN], sc1[TN];
+  f16x8 af[2][TM], bf[2][TN];
+
+  // Reads of a stage's weight chunk / scales and its sub-step 0 operands
+  // into buffer 0.
+  auto load_first = [&](const Stage& stg) {
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
       wr[t] = stg.w[w_slot[t]];
@@ -245,34 +257,30 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
       sc0[t] = f16x2{s2.x, s2.x};
       sc1[t] = f16x2{s2.y, s2.y};
     }
-    f16x8 af[2][TM], bf[2][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i) af[0][i] = __builtin_bit_cast(f16x8, stg.a[a_row8[i] + ((4 * g) ^ a_sw)]);
 #pragma unroll
     for (int t = 0; t < TN; ++t) bf[0][t] = unpack8_f16(wr[t][0], sc0[t]);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int cb = s & 1, nb = cb ^ 1;
-      if (s < 3) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-          af[nb][i] = __builtin_bit_cast(f16x8, stg.a[a_row8[i] + ((4 * g + s + 1) ^ a_sw)]);
-#pragma unroll
-        for (int t = 0; t < TN; ++t) bf[nb][t] = unpack8_f16(wr[t][s + 1], s + 1 < 2 ? sc0[t] : sc1[t]);
-      }
+  };
+  // MFMAs of sub-step s (operands in buffer s & 1); for s < 3 the operands of
+  // s + 1 are read and unpacked meanwhile (sched_group_barrier pins the
+  // interleave: each MFMA is followed by one LDS read and a few VALU ops).
+  constexpr int kMFMA = 0x008, kVALU = 0x002, kDSR = 0x100;
+  auto substep = [&](const Stage& stg, int s) {
+    const int cb = s & 1, nb = cb ^ 1;
+    if (s < 3) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
+        af[nb][i] = __builtin_bit_cast(f16x8, stg.a[a_row8[i] + ((4 * g + s + 1) ^ a_sw)]);
 #pragma unroll
-        for (int t = 0; t < TN; ++t)
-          acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cb][i], bf[cb][t], acc[i][t], 0, 0, 0);
+      for (int t = 0; t < TN; ++t) bf[nb][t] = unpack8_f16(wr[t][s + 1], s + 1 < 2 ? sc0[t] : sc1[t]);
     }
-    // schedule: operand reads and sub-step 0 unpack, then per sub-step the
-    // MFMAs interleaved with the next sub-step's reads and unpack
-    constexpr int kMFMA = 0x008, kVALU = 0x002, kDSR = 0x100;
-    __builtin_amdgcn_sched_group_barrier(kDSR, 2 * TN + TM, 0);
-    __builtin_amdgcn_sched_group_barrier(kVALU, 8 * TN + 4, 0);
 #pragma unroll
-    for (int s = 0; s < 3; ++s) {
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int t = 0; t < TN; ++t)
+        acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cb][i], bf[cb][t], acc[i][t], 0, 0, 0);
+    if (s < 3) {
 #pragma unroll
       for (int q = 0; q < TM * TN; ++q) {
         __builtin_amdgcn_sched_group_barrier(kMFMA, 1, 0);
@@ -280,31 +288,56 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
         if (q < 4) __builtin_amdgcn_sched_group_barrier(kVALU, 2 * TN, 0);
       }
     }
-    __builtin_amdgcn_sched_group_barrier(kMFMA, TM * TN, 0);
   };
 
-  // Step kt: operands of kt in stage `cur`; stage `nxt2` (read last in step
-  // kt-1) receives kt+2.  After the DMA of kt this lane issued those of kt+1.
-  auto step = [&](int kt, const Stage& cur, Stage& nxt2) {
+  // Step kt (stage `cur` holds kt, `nxt` holds kt+1): sub-steps 0..2; then,
+  // once every wave's reads of `cur` are done, the barrier that also
+  // publishes `nxt`, the DMA of kt+3 into `cur`, and sub-step 3 overlapped
+  // with the reads and first unpack of `nxt`.  Issued after the DMA of kt+1:
+  // that of kt+2.
+  auto step = [&](int kt, Stage& cur, const Stage& nxt) {
+    substep(cur, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    substep(cur, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    substep(cur, 2);
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(VM_STEP));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    dma(nxt2, kt + 2);
+    dma(cur, kt + 3);
     __builtin_amdgcn_sched_barrier(0);
-    compute(cur);
+    // sub-step 3 uses buffer 1; the next stage's first operands go to buffer 0
+    substep(cur, 3);
+    load_first(nxt);
+    // reads first (one per MFMA), the unpack in the second half
+    constexpr int kReads = TM + 2 * TN, kMF = TM * TN;
+#pragma unroll
+    for (int q = 0; q < kMF; ++q) {
+      __builtin_amdgcn_sched_group_barrier(kMFMA, 1, 0);
+      if (q < kReads) __builtin_amdgcn_sched_group_barrier(kDSR, 1, 0);
+      if (q >= kMF / 2) __builtin_amdgcn_sched_group_barrier(kVALU, (8 * TN + 6 + kMF / 2 - 1) / (kMF / 2), 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
   };
 
   dma(st0, 0);
   dma(st1, 1);
+  dma(st2, 2);
+  // stage 0 complete (two DMA groups issued after it), then published
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * VM_STEP));
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  load_first(st0);
+  __builtin_amdgcn_sched_barrier(0);
   int kt = 0;
   for (; kt + 3 <= KT; kt += 3) {
-    step(kt + 0, st0, st2);
-    step(kt + 1, st1, st0);
-    step(kt + 2, st2, st1);
+    step(kt + 0, st0, st1);
+    step(kt + 1, st1, st2);
+    step(kt + 2, st2, st0);
   }
-  if (kt + 0 < KT) step(kt + 0, st0, st2);
-  if (kt + 1 < KT) step(kt + 1, st1, st0);
+  if (kt + 0 < KT) step(kt + 0, st0, st1);
+  if (kt + 1 < KT) step(kt + 1, st1, st2);
   // Drain the DMA still in flight into LDS before the workgroup exits.
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
 
