@@ -42,6 +42,7 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-peaks", action="store_true", help="skip the measured copy and bf16 GEMM reference rates")
     p.add_argument("--phases", default="quantize,gemv,gemm",
                    help="comma list of quantize, gemv, gemm (= prefill + dit), prefill, dit")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -332,17 +333,24 @@ def main():
     fracs = [comps[k] for k in ("quantize_hbm_frac", "gemv_hbm_frac", "gemm_mfma_frac") if k in comps]
     value = 100.0 * sum(fracs) / len(fracs) if fracs else 0.0
 
-    # dominant kernel: the stage with the largest share of the step time
-    dom = max(names, key=lambda k: per[k]["us"])
+    # dominant kernel: the kernel family with the largest share of the step
+    # time (stages grouped by the kernel that does their work), measured on
+    # its representative single-launch stage
+    family = {"quantize_mse": "mse", "quantize_absmax_pass": "absmax", "quantize_absmax_dynamic": "absmax"}
+    share = {}
+    for k in names:
+        f = family.get(k, "gemm" if k.startswith("gemm_") else "gemv" if k.startswith("gemv_") else k)
+        share[f] = share.get(f, 0.0) + per[k]["us"]
+    representative = {"mse": "quantize_mse", "absmax": "quantize_absmax_pass", "gemm": "gemm_prefill_up_reuse"}
+    top = max(share, key=share.get)
+    dom = representative.get(top, top)
     roofline = None
     kernel_of = {
         "quantize_mse": ("quantize_mse_kernel", "alu"),
         "quantize_absmax_pass": ("quantize_absmax_kernel", "hbm"),
         "gemm_prefill_up_reuse": ("gemm_w4a4_kernel<256,256>", "mfma"),
     }
-    if dom.startswith("gemm_"):
-        dom = "gemm_prefill_up_reuse" if "gemm_prefill_up_reuse" in per else dom
-    if dom in kernel_of:
+    if dom in kernel_of and dom in per:
         kname, bound = kernel_of[dom]
         g, calls, nbytes, flops, ops = stages[dom]
         t = per[dom]["us"] / 1e6
@@ -357,6 +365,15 @@ def main():
             roofline = {"bound": "hbm", "kernel": kname, "achieved": nbytes / t / 1e9, "peak": 8000.0,
                         "unit": "GB/s", "frac": nbytes / t / HBM_PEAK, "traffic": None}
         roofline["launch_us"] = per[dom]["us_per_call"] if calls == 1 else per[dom]["us"]
+
+    peaks = None if args.no_peaks else measured_peaks(torch, dev)
+    if roofline is not None:
+        ref = None
+        if peaks and roofline["bound"] == "mfma":
+            ref = peaks["bf16_gemm_TFLOP_s"]
+        elif peaks and roofline["bound"] == "hbm":
+            ref = peaks["hbm_copy_GB_s"]
+        roofline["frac_vs_measured"] = roofline["achieved"] / ref if ref else None
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(comps)
 
@@ -377,9 +394,58 @@ def main():
         "components": {k: round(v, 5) for k, v in comps.items()},
         "stages": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in per.items()},
         "roofline": roofline,
+        "measured_peaks": peaks,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def measured_peaks(torch, dev):
+    """Rates this GPU reaches on plain work, next to the datasheet peaks: a
+    1 GiB device-to-device copy (read + write bytes) and a bf16 8192^3 matrix
+    product through torch (the vendor GEMM library)."""
+    out = {}
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    best = None
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / 1e3
+        best = t if best is None else min(best, t)
+    out["hbm_copy_GB_s"] = 2.0 * n / best / 1e9
+    del src, dst
+    a = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    c = a @ b
+    best = None
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        c = a @ b
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / 1e3
+        best = t if best is None else min(best, t)
+    out["bf16_gemm_TFLOP_s"] = 2.0 * 8192 ** 3 / best / 1e12
+    del a, b, c
+    torch.cuda.synchronize()
+    return {k: round(v, 1) for k, v in out.items()}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(gpu_comps):
@@ -424,6 +490,7 @@ def cpu_baseline(gpu_comps):
     res["gemm_GFLOP_s"] = flops / dt / 1e9
     value = 100.0 * (qfrac + gfrac + mfrac) / 3
     return {"value": value, "unit": "% of MI355X peak (same formula as value)", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": "absmax quantize of the 4096x4096 fp32 q tensor (with amax), MSE of 256x4096, "
                       "W4A16 M=1 x 4096x4096 weight, W4A4 128x1024 outputs of the prefill product (K=4096)",
             "components": {k: round(v, 4) for k, v in res.items()}}
