@@ -18,6 +18,7 @@ _lib = None
 
 ABSMAX = 0
 MSE = 1
+FOUR_OVER_SIX = 2
 
 
 def _load():
@@ -47,6 +48,8 @@ def _load():
     lib.oracle_absmax_scale_code.argtypes = [P, ctypes.c_float]
     lib.oracle_mse_scale_code.restype = ctypes.c_int
     lib.oracle_mse_scale_code.argtypes = [P, ctypes.c_float]
+    lib.oracle_4o6_scale_code.restype = ctypes.c_int
+    lib.oracle_4o6_scale_code.argtypes = [P, ctypes.c_float]
     lib.oracle_block_error.restype = ctypes.c_double
     lib.oracle_block_error.argtypes = [P, ctypes.c_float, ctypes.c_int]
     lib.oracle_quantize.restype = ctypes.c_int
@@ -107,6 +110,11 @@ def absmax_scale_code(block, sg):
 def mse_scale_code(block, sg):
     b = np.ascontiguousarray(block, dtype=np.float32).reshape(16)
     return _load().oracle_mse_scale_code(_ptr(b), float(np.float32(sg)))
+
+
+def four_over_six_scale_code(block, sg):
+    b = np.ascontiguousarray(block, dtype=np.float32).reshape(16)
+    return _load().oracle_4o6_scale_code(_ptr(b), float(np.float32(sg)))
 
 
 def block_error(block, sg, scale_code):

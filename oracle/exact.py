@@ -124,3 +124,15 @@ def mse_search(block, sg):
             if best is None or err < best_err:
                 best, best_err = v, err
     return best, best_err, gbest, gbest_err
+
+
+def four_over_six(block, sg):
+    """Exact four-over-six choice: the E4M3 roundings of max|W| / (6 s_g) and
+    max|W| / (4 s_g); the smaller exact error wins and a tie keeps the
+    smaller scale.  Returns (scale, error)."""
+    m = max(abs(F(w)) for w in block)
+    c6 = round_format(m / (6 * F(sg)), 3, -6, E4M3_MAX)
+    c4 = round_format(m / (4 * F(sg)), 3, -6, E4M3_MAX)
+    e6 = block_error(block, c6, sg)
+    e4 = block_error(block, c4, sg)
+    return (c4, e4) if e4 < e6 else (c6, e6)

@@ -1,6 +1,7 @@
 /*
  * NVFP4 reference oracle: a plain, slow, obviously-correct CPU implementation
- * of the NVFP4 block quantizer (absmax and MSE block scales), dequantization,
+ * of the NVFP4 block quantizer (absmax, MSE and four-over-six block scales),
+ * dequantization,
  * and the W4A16 / W4A4 dot products, all in IEEE fp64.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
@@ -28,6 +29,8 @@
  *   (E2M1 and E4M3), E4M3 saturates at 448.              R5 MSE candidates: the
  *   E4M3 values in [a/2, min(2a, 448)] plus the absmax scale; error = fp64
  *   sequential sum of rounded squares; ties keep the smaller scale.
+ *   R11 four-over-six: candidates max/(6 s_g) and max/(4 s_g), each rounded
+ *   to E4M3; the R5 error decides, ties keep the smaller scale.
  */
 #include <math.h>
 #include <stdint.h>
@@ -171,11 +174,27 @@ int oracle_mse_scale_code(const float* w, float sg) {
     return best;
 }
 
+/* Four-over-six block scale code [P1 sec.2, algorithm table: each block
+ * chooses between two possible largest values, 4 or 6, whichever gives the
+ * smaller error].  Reading R11: the two candidates are the nearest E4M3
+ * values to max|W| / (6 s_g) (the absmax scale: the block maximum lands on
+ * 6) and to max|W| / (4 s_g) (it lands on 4); the error is the MSE
+ * objective's (R5) and a tie keeps the smaller scale, i.e. the first. */
+int oracle_4o6_scale_code(const float* w, float sg) {
+    double m = block_amax(w);
+    int c6 = oracle_e4m3_nearest(m / (6.0 * (double)sg));
+    int c4 = oracle_e4m3_nearest(m / (4.0 * (double)sg));
+    if (c4 == c6) return c6;
+    double e6 = oracle_block_error(w, sg, c6);
+    double e4 = oracle_block_error(w, sg, c4);
+    return e4 < e6 ? c4 : c6;
+}
+
 /* ---- whole tensors ---------------------------------------------------- */
 
 /* Quantize a row-major [rows, cols] fp32 tensor (cols % 16 == 0; bf16 inputs
  * are passed here widened to fp32, which is exact).
- *   method 0 = absmax, 1 = MSE.
+ *   method 0 = absmax, 1 = MSE, 2 = four-over-six.
  *   *sg: if sg_given, read; else written with oracle_global_scale(amax).
  *   codes [rows, cols/2]: byte i = code(W[2i]) | code(W[2i+1]) << 4 (R1).
  *   scales [rows, cols/16]: E4M3 byte of each block's scale.
@@ -190,7 +209,8 @@ int oracle_quantize(int method, const float* x, int64_t rows, int64_t cols,
     #pragma omp parallel for schedule(static) num_threads(threads > 0 ? threads : 1)
     for (int64_t b = 0; b < nblocks; ++b) {
         const float* w = x + 16 * b;
-        int sc = method == 0 ? oracle_absmax_scale_code(w, s_g) : oracle_mse_scale_code(w, s_g);
+        int sc = method == 0 ? oracle_absmax_scale_code(w, s_g)
+               : method == 1 ? oracle_mse_scale_code(w, s_g) : oracle_4o6_scale_code(w, s_g);
         uint8_t code[16];
         encode_block(w, oracle_e4m3_value(sc), s_g, code);
         scales[b] = (uint8_t)sc;

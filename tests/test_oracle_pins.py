@@ -198,6 +198,49 @@ def test_mse_matches_exact_bruteforce_and_beats_absmax():
     print(f"blocks whose unrestricted optimum lies outside [a/2, 2a]: {outside}/{len(x)}")
 
 
+def test_four_over_six_matches_exact_and_never_worse_than_absmax():
+    x = _blocks_tiny(5, 64)
+    sg = F(oracle.global_scale(float(np.abs(x).max())))
+    picked_four = 0
+    for blk_np in x:
+        blk = [F(float(v)) for v in blk_np]
+        best, best_err = exact.four_over_six(blk, sg)
+        code = oracle.four_over_six_scale_code(blk_np, float(sg))
+        chosen = exact.E4M3[code]
+        chosen_err = exact.block_error(blk, chosen, sg)
+        # the oracle's fp64 choice is the exact choice, or an exact-or-rounding tie of it
+        assert chosen == best or abs(chosen_err - best_err) <= best_err * F(1, 10 ** 12), (code, best)
+        abs_scale = exact.absmax_scale(blk, sg)
+        assert chosen_err <= exact.block_error(blk, abs_scale, sg)
+        picked_four += chosen != abs_scale
+    assert picked_four > 0          # the second candidate does win on some blocks
+
+
+def test_four_over_six_worked_block():
+    # s_g = 1, one 6.0 and fifteen 5.0.  Max -> 6 (scale 1.0, code 0x38): each
+    # 5 sits on the 4|6 midpoint and rounds to the even code (4), error 1 each,
+    # total 15.  Max -> 4 (scale 1.5, code 0x3C): 5 / 1.5 = 3.33 -> 3, i.e.
+    # 4.5, error 0.25 each, total 3.75; the 6 maps to 4 exactly.  Four wins.
+    blk = np.full(16, 5.0, dtype=np.float32)
+    blk[0] = 6.0
+    assert oracle.block_error(blk, 1.0, 0x38) == 15.0
+    assert oracle.block_error(blk, 1.0, 0x3C) == 3.75
+    assert oracle.four_over_six_scale_code(blk, 1.0) == 0x3C
+    # sixteen 6.0: both candidates reconstruct exactly -> tie -> the smaller scale
+    assert oracle.four_over_six_scale_code(np.full(16, 6.0, dtype=np.float32), 1.0) == 0x38
+    # all-zero block: scale 0
+    assert oracle.four_over_six_scale_code(np.zeros(16, dtype=np.float32), 1.0) == 0
+
+
+def test_four_over_six_tensor_method_matches_block_function():
+    x = _blocks_tiny(6, 32).reshape(8, 64)
+    c, s, sg = oracle.quantize(x, oracle.FOUR_OVER_SIX)
+    for r in range(8):
+        for b in range(4):
+            blk = x[r, 16 * b:16 * b + 16]
+            assert s[r, b] == oracle.four_over_six_scale_code(blk, sg)
+
+
 def test_mse_window_bounds_are_exact_e4m3_steps():
     # a block whose a = amax/(6 s_g) is itself an E4M3 value: the window holds
     # exactly 17 candidates (a/2 .. 2a inclusive) in the normal range.
