@@ -154,35 +154,44 @@ def main():
                      torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev),
                      torch.empty(1, dtype=torch.float32, device=dev))
             out_m = (torch.empty_like(out_a[0]), torch.empty_like(out_a[1]), torch.empty_like(out_a[2]))
+            out_f = (torch.empty_like(out_a[0]), torch.empty_like(out_a[1]), torch.empty_like(out_a[2]))
             ws = torch.empty(nv.workspace_bytes(nv.OP_QUANTIZE, rows, cols), dtype=torch.uint8, device=dev)
             nv.quantize_absmax(xd, workspace=ws, out=out_a)
             torch.cuda.synchronize()
             sg = float(out_a[2].item())
             out_m[2].fill_(sg)
-            qbuf.append((xd, out_a, out_m, ws, sg, rows, cols))
+            out_f[2].fill_(sg)
+            qbuf.append((xd, out_a, out_m, out_f, ws, sg, rows, cols))
             layer_elems += rows * cols
             mse_ops += mse_candidates(w, sg) * 16 * 6.0
             del w
         n = layer_elems
 
         def q_dynamic():
-            for xd, out_a, out_m, ws, sg, rows, cols in qbuf:
+            for xd, out_a, out_m, out_f, ws, sg, rows, cols in qbuf:
                 nv.quantize_absmax(xd, workspace=ws, out=out_a)
 
         def q_pass():
-            for xd, out_a, out_m, ws, sg, rows, cols in qbuf:
+            for xd, out_a, out_m, out_f, ws, sg, rows, cols in qbuf:
                 nv.lib().nvfp4_quantize_absmax(nv._ptr(xd), nv.F32, rows, cols, nv._ptr(out_a[0]),
                                                nv._ptr(out_a[1]), nv._ptr(out_a[2]), nv.GLOBAL_GIVEN, None, 0,
                                                nv._stream())
 
         def q_mse():
-            for xd, out_a, out_m, ws, sg, rows, cols in qbuf:
+            for xd, out_a, out_m, out_f, ws, sg, rows, cols in qbuf:
                 nv.lib().nvfp4_quantize_mse(nv._ptr(xd), nv.F32, rows, cols, nv._ptr(out_m[0]), nv._ptr(out_m[1]),
                                             nv._ptr(out_m[2]), nv.GLOBAL_GIVEN, None, 0, nv._stream())
+
+        def q_4o6():
+            for xd, out_a, out_m, out_f, ws, sg, rows, cols in qbuf:
+                nv.lib().nvfp4_quantize_4o6(nv._ptr(xd), nv.F32, rows, cols, nv._ptr(out_f[0]), nv._ptr(out_f[1]),
+                                            nv._ptr(out_f[2]), nv.GLOBAL_GIVEN, None, 0, nv._stream())
 
         capture("quantize_absmax_dynamic", q_dynamic, nbytes=n * (4 + 4 + 0.5625))
         capture("quantize_absmax_pass", q_pass, nbytes=n * (4 + 0.5625))
         capture("quantize_mse", q_mse, nbytes=n * (4 + 0.5625), ops=mse_ops)
+        # four-over-six: at most 2 candidates per block, 16 elements x 6 ops each
+        capture("quantize_4o6", q_4o6, nbytes=n * (4 + 0.5625), ops=n / 16 * 2 * 16 * 6.0)
 
     # ------------------------------------------------------------ gemv
     if "gemv" in phases:
@@ -336,7 +345,8 @@ def main():
     # dominant kernel: the kernel family with the largest share of the step
     # time (stages grouped by the kernel that does their work), measured on
     # its representative single-launch stage
-    family = {"quantize_mse": "mse", "quantize_absmax_pass": "absmax", "quantize_absmax_dynamic": "absmax"}
+    family = {"quantize_mse": "mse", "quantize_4o6": "mse", "quantize_absmax_pass": "absmax",
+              "quantize_absmax_dynamic": "absmax"}
     share = {}
     for k in names:
         f = family.get(k, "gemm" if k.startswith("gemm_") else "gemv" if k.startswith("gemv_") else k)

@@ -4,7 +4,7 @@
 // distinto", section 2 ("NVFP4 sin vLLM: torch._scaled_mm a mano"): the
 // activation is quantized to NVFP4 on every call, 16-element block by block
 // with the absmax criterion, and out = (A s_a)(B s_b)^T is returned in 16-bit
-// precision (a "4-bit island with BF16 shores").
+// precision, so each quantized layer takes and returns 16-bit tensors.
 //
 // Design (gfx950):
 //  * act_quant: absmax NVFP4 quantization of A (same encoder as the weight

@@ -14,8 +14,8 @@ hipError_t launch_global_scale(const void* x, bool bf16, int64_t n_elems, float*
                                hipStream_t stream);
 hipError_t launch_quantize_absmax(const void* x, bool bf16, int64_t n_elems, const float* sg, uint8_t* codes,
                                   uint8_t* scales, hipStream_t stream);
-hipError_t launch_quantize_mse(const void* x, bool bf16, int64_t n_elems, const float* sg, uint8_t* codes,
-                               uint8_t* scales, hipStream_t stream);
+hipError_t launch_quantize_search(const void* x, bool bf16, bool four_over_six, int64_t n_elems, const float* sg,
+                                  uint8_t* codes, uint8_t* scales, hipStream_t stream);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* sg, int64_t n_elems,
                           void* out, bool bf16_out, hipStream_t stream);
 hipError_t launch_gemv_w4a16(const uint16_t* x, const uint8_t* codes, const uint8_t* scales, const float* sg,

@@ -11,7 +11,7 @@ namespace {
 
 using namespace nvfp4;
 
-constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -46,7 +46,9 @@ int validate_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, co
   return NVFP4_OK;
 }
 
-int quantize_common(bool mse, const void* x, int x_dtype, int64_t rows, int64_t cols, uint8_t* codes,
+enum class Search { kAbsmax, kMse, kFourOverSix };
+
+int quantize_common(Search mode, const void* x, int x_dtype, int64_t rows, int64_t cols, uint8_t* codes,
                     uint8_t* scales, float* gs, int flags, void* ws, size_t ws_bytes, void* stream) {
   int st = validate_quantize(x, x_dtype, rows, cols, codes, scales, gs, flags, ws, ws_bytes);
   if (st != NVFP4_OK) return st;
@@ -58,8 +60,9 @@ int quantize_common(bool mse, const void* x, int x_dtype, int64_t rows, int64_t 
     hipError_t e = launch_global_scale(x, bf16, n, reinterpret_cast<float*>(ws), gs, s);
     if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
   }
-  hipError_t e = mse ? launch_quantize_mse(x, bf16, n, gs, codes, scales, s)
-                     : launch_quantize_absmax(x, bf16, n, gs, codes, scales, s);
+  hipError_t e = mode == Search::kAbsmax
+                     ? launch_quantize_absmax(x, bf16, n, gs, codes, scales, s)
+                     : launch_quantize_search(x, bf16, mode == Search::kFourOverSix, n, gs, codes, scales, s);
   return launch_status(e);
 }
 
@@ -102,14 +105,20 @@ size_t nvfp4_workspace_bytes(int op, int64_t a, int64_t b) {
 int nvfp4_quantize_absmax(const void* x, int x_dtype, int64_t rows, int64_t cols, uint8_t* codes,
                           uint8_t* scales, float* global_scale, int flags, void* workspace, size_t ws_bytes,
                           void* stream) {
-  return quantize_common(false, x, x_dtype, rows, cols, codes, scales, global_scale, flags, workspace, ws_bytes,
-                         stream);
+  return quantize_common(Search::kAbsmax, x, x_dtype, rows, cols, codes, scales, global_scale, flags, workspace,
+                         ws_bytes, stream);
 }
 
 int nvfp4_quantize_mse(const void* x, int x_dtype, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
                        float* global_scale, int flags, void* workspace, size_t ws_bytes, void* stream) {
-  return quantize_common(true, x, x_dtype, rows, cols, codes, scales, global_scale, flags, workspace, ws_bytes,
-                         stream);
+  return quantize_common(Search::kMse, x, x_dtype, rows, cols, codes, scales, global_scale, flags, workspace,
+                         ws_bytes, stream);
+}
+
+int nvfp4_quantize_4o6(const void* x, int x_dtype, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                       float* global_scale, int flags, void* workspace, size_t ws_bytes, void* stream) {
+  return quantize_common(Search::kFourOverSix, x, x_dtype, rows, cols, codes, scales, global_scale, flags,
+                         workspace, ws_bytes, stream);
 }
 
 int nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const float* global_scale, int64_t rows,

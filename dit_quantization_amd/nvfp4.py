@@ -24,6 +24,7 @@ _P, _I, _I64, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size
 SIGNATURES = {
     "nvfp4_quantize_absmax": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _I, _P, _SZ, _P]),
     "nvfp4_quantize_mse": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _I, _P, _SZ, _P]),
+    "nvfp4_quantize_4o6": (_I, [_P, _I, _I64, _I64, _P, _P, _P, _I, _P, _SZ, _P]),
     "nvfp4_dequant": (_I, [_P, _P, _P, _I64, _I64, _P, _I, _P]),
     "nvfp4_gemv_w4a16": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _SZ, _P]),
     "nvfp4_gemm_w4a4": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _I, _P, _SZ, _P]),
@@ -138,6 +139,11 @@ def quantize_absmax(x, global_scale=None, workspace=None, out=None):
 def quantize_mse(x, global_scale=None, workspace=None, out=None):
     """NVFP4 quantization with MSE-searched block scales (same layout)."""
     return _quantize("nvfp4_quantize_mse", x, global_scale, workspace, out)
+
+
+def quantize_4o6(x, global_scale=None, workspace=None, out=None):
+    """NVFP4 quantization with four-over-six block scales (same layout)."""
+    return _quantize("nvfp4_quantize_4o6", x, global_scale, workspace, out)
 
 
 def dequant(codes, scales, global_scale, out_dtype=torch.float32, out=None):

@@ -99,14 +99,31 @@ int nvfp4_quantize_absmax(const void* x, int x_dtype, int64_t rows, int64_t cols
 /*
  * nvfp4_quantize_mse -- NVFP4 encoding with MSE-searched block scales.
  * ("Tu pipeline NVFP4 ...", section 2, box "Derivacion del objetivo de
- * optimizacion MSE vs Absmax": s_b* = argmin over s_b of
- * sum_k (W_k - s_b s_g Q(W_k / (s_b s_g)))^2; the algorithm table: "tries
- * several scales and keeps the one that minimises the block's
- * reconstruction error".)  Same arguments and layout as
- * nvfp4_quantize_absmax; candidate set and arithmetic in the header comment.
- * The chosen block error is never larger than the absmax scale's error.
+ * optimizacion MSE vs Absmax": the block scale is the argmin over s_b of
+ * sum_k (W_k - s_b s_g Q(W_k / (s_b s_g)))^2; the algorithm table: several
+ * candidate scales are tried and the one with the least block
+ * reconstruction error is kept.)  Same arguments and layout as
+ * nvfp4_quantize_absmax.  Candidates: the absmax scale plus every positive
+ * E4M3 value c with a/2 <= c <= min(2a, 448), a = max|W| / (6 s_g).  Error:
+ * d_k = |W_k| - c s_g |q_k| rounded once in fp64, E = fp64 sum of the
+ * rounded squares in element order; candidates in ascending order, replaced
+ * only on a strictly smaller error.  The chosen block error is never larger
+ * than the absmax scale's error.
  */
 int nvfp4_quantize_mse(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                       uint8_t* codes, uint8_t* scales, float* global_scale,
+                       int flags, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * nvfp4_quantize_4o6 -- NVFP4 encoding with four-over-six block scales
+ * ("Tu pipeline NVFP4 ...", section 2, algorithm table: every block picks
+ * between two largest representable values, 4 or 6, whichever reconstructs
+ * it with the smaller error).  Same arguments and layout as
+ * nvfp4_quantize_absmax.  Candidates: the nearest E4M3 values to
+ * max|W| / (6 s_g) (the absmax scale) and to max|W| / (4 s_g); the error
+ * and tie rule are nvfp4_quantize_mse's (a tie keeps the absmax scale).
+ */
+int nvfp4_quantize_4o6(const void* x, int x_dtype, int64_t rows, int64_t cols,
                        uint8_t* codes, uint8_t* scales, float* global_scale,
                        int flags, void* workspace, size_t ws_bytes, void* stream);
 

@@ -155,8 +155,8 @@ double oracle_block_error(const float* w, float sg, int scale_code) {
 }
 
 /* MSE block scale code [P1 sec.2 MSE objective and the algorithm table:
- * "tries several scales and keeps the one with the smallest reconstruction
- * error"].  Candidates (reading R5): the absmax scale plus every positive
+ * several scales are tried and the one with the least reconstruction error
+ * of the block wins].  Candidates (reading R5): the absmax scale plus every positive
  * E4M3 value c with a/2 <= c <= min(2a, 448), a = max|W|/(6 s_g); visited in
  * ascending order, replaced only on a strictly smaller error. */
 int oracle_mse_scale_code(const float* w, float sg) {
@@ -240,8 +240,8 @@ static double wq(const uint8_t* codes, const uint8_t* scales, float sg, int64_t 
     return oracle_e2m1_value(code) * oracle_e4m3_value(scales[i / 16]) * (double)sg;
 }
 
-/* W4A16 dot products [P1 sec.2 "W4A16 keeps 4-bit weights and unpacks them to
- * 16 bits to multiply"]: y*[m,n] = sum_k x[m,k] * W^[n,k] in fp64 for each
+/* W4A16 dot products [P1 sec.2: in W4A16 the weights stay in 4 bits and are
+ * widened to 16 bits for the multiply]: y*[m,n] = sum_k x[m,k] * W^[n,k] in fp64 for each
  * requested (m, n) pair, with tau = 1e-5 * sum_k |x[m,k]| |W^[n,k]|. */
 int oracle_dot_w4a16(const float* x, const uint8_t* w_codes, const uint8_t* w_scales, float sgw,
                      int64_t K, const int64_t* pm, const int64_t* pn, int64_t npairs,

@@ -25,14 +25,14 @@ def header_functions():
 def test_library_exports_every_declared_symbol():
     L = nv.lib()
     names = header_functions()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     for n in names:
         assert hasattr(L, n), n
         assert n in nv.SIGNATURES, n
 
 
 def test_status_strings_and_version():
-    assert nv.lib().nvfp4_version() == 10000
+    assert nv.lib().nvfp4_version() == 10100
     for s in range(9):
         assert nv.status_string(s) and nv.status_string(s) != "unknown status"
     assert nv.status_string(99) == "unknown status"
@@ -51,7 +51,7 @@ def q(fn, x=A16, dt=nv.F32, rows=4, cols=64, codes=A16, scales=A16, gs=A4, flags
     return getattr(nv.lib(), fn)(x, dt, rows, cols, codes, scales, gs, flags, ws, wsb, None)
 
 
-@pytest.mark.parametrize("fn", ["nvfp4_quantize_absmax", "nvfp4_quantize_mse"])
+@pytest.mark.parametrize("fn", ["nvfp4_quantize_absmax", "nvfp4_quantize_mse", "nvfp4_quantize_4o6"])
 def test_quantize_validation(fn):
     assert q(fn, x=None) == nv.ERR_NULL
     assert q(fn, codes=None) == nv.ERR_NULL

@@ -13,7 +13,8 @@ pytestmark = pytest.mark.gpu
 
 
 def _gpu_quant(method, x_dev, sg=None):
-    fn = nv.quantize_absmax if method == oracle.ABSMAX else nv.quantize_mse
+    fn = {oracle.ABSMAX: nv.quantize_absmax, oracle.MSE: nv.quantize_mse,
+          oracle.FOUR_OVER_SIX: nv.quantize_4o6}[method]
     c, s, g = fn(x_dev, global_scale=sg)
     torch.cuda.synchronize()
     return host(c), host(s), float(host(g)[0])
@@ -44,14 +45,14 @@ def _adversarial(rows, cols, seed):
 SHAPES = [(1, 32), (3, 96), (37, 160), (129, 4096), (5, 14336)]
 
 
-@pytest.mark.parametrize("method", [oracle.ABSMAX, oracle.MSE])
+@pytest.mark.parametrize("method", [oracle.ABSMAX, oracle.MSE, oracle.FOUR_OVER_SIX])
 @pytest.mark.parametrize("shape", SHAPES)
 def test_quantize_fp32_random_shapes(method, shape):
     x = _adversarial(*shape, seed=shape[0] * 7 + shape[1])
     _check(method, x, dev_f32(x), what=f"fp32 {shape}")
 
 
-@pytest.mark.parametrize("method", [oracle.ABSMAX, oracle.MSE])
+@pytest.mark.parametrize("method", [oracle.ABSMAX, oracle.MSE, oracle.FOUR_OVER_SIX])
 @pytest.mark.parametrize("shape", [(2, 64), (33, 480), (64, 3072)])
 def test_quantize_bf16(method, shape):
     a = inputs.normal_f32(shape, 100 + shape[0])
@@ -60,14 +61,14 @@ def test_quantize_bf16(method, shape):
     _check(method, inputs.bf16_bits_to_f32(bits), dev_bf16(bits), what=f"bf16 {shape}")
 
 
-@pytest.mark.parametrize("method", [oracle.ABSMAX, oracle.MSE])
+@pytest.mark.parametrize("method", [oracle.ABSMAX, oracle.MSE, oracle.FOUR_OVER_SIX])
 @pytest.mark.parametrize("sg", [1.0, 1e-3, 37.5, 1e-30])
 def test_quantize_given_global_scale(method, sg):
     x = _adversarial(8, 256, seed=int(sg * 1000) % 97)
     _check(method, x, dev_f32(x), sg=sg, what=f"given sg {sg}")
 
 
-@pytest.mark.parametrize("method", [oracle.ABSMAX, oracle.MSE])
+@pytest.mark.parametrize("method", [oracle.ABSMAX, oracle.MSE, oracle.FOUR_OVER_SIX])
 def test_quantize_exact_ties(method):
     # s_g = 1 given; elements on every E2M1 midpoint of several scales, and
     # block maxima on E4M3 midpoints
@@ -105,15 +106,16 @@ def test_tiny_config_quantize():
     _check(oracle.ABSMAX, w, dev_f32(w), what="tiny 256x256")
 
 
+@pytest.mark.parametrize("method", [oracle.MSE, oracle.FOUR_OVER_SIX])
 @pytest.mark.parametrize("name", ["q", "k", "down"])
-def test_layerset_mse_full_size_sampled_rows(name):
+def test_layerset_search_full_size_sampled_rows(name, method):
     (_, w), = list(inputs.layerset([name]))
-    print(f"[case] layerset {name} {w.shape}", flush=True)
-    gc, gs, gg = _gpu_quant(oracle.MSE, dev_f32(w))
+    print(f"[case] layerset {name} {w.shape} method {method}", flush=True)
+    gc, gs, gg = _gpu_quant(method, dev_f32(w))
     sg = oracle.global_scale(float(np.abs(w).max()))
     assert gg == sg
     rows = np.unique(np.concatenate([[0, w.shape[0] - 1], inputs.rng(5).choice(w.shape[0], 48, replace=False)]))
-    oc, os_, _ = oracle.quantize(w[rows], oracle.MSE, sg=sg)
+    oc, os_, _ = oracle.quantize(w[rows], method, sg=sg)
     assert np.array_equal(gs[rows], os_)
     assert np.array_equal(gc[rows], oc)
 
