@@ -48,6 +48,8 @@ def _load():
     lib.oracle_absmax_scale_code.argtypes = [P, ctypes.c_float]
     lib.oracle_mse_scale_code.restype = ctypes.c_int
     lib.oracle_mse_scale_code.argtypes = [P, ctypes.c_float]
+    lib.oracle_lora_term.restype = ctypes.c_int
+    lib.oracle_lora_term.argtypes = [P, P, P, i64, i64, P, P, i64, P, P, ctypes.c_int]
     lib.oracle_4o6_scale_code.restype = ctypes.c_int
     lib.oracle_4o6_scale_code.argtypes = [P, ctypes.c_float]
     lib.oracle_block_error.restype = ctypes.c_double
@@ -198,6 +200,28 @@ def dot_w4a4(a_codes, a_scales, sga, w_codes, w_scales, sgw, K, pairs=None, M=No
                                  _threads(threads))
     if rc != 0:
         raise ValueError("oracle_dot_w4a4: bad shape")
+    return y, tau
+
+
+def lora_term(x, A, B, pairs=None, threads=None):
+    """fp64 low-rank term y*_L[m,n] = sum_j (x A^T)[m,j] B[n,j] and its
+    tolerance for the requested (m, n) pairs (all pairs if None).  x [M, K],
+    A [r, K], B [N, r]: 16-bit values as float32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    A = np.ascontiguousarray(A, dtype=np.float32)
+    B = np.ascontiguousarray(B, dtype=np.float32)
+    M, K = x.shape
+    r = A.shape[0]
+    N = B.shape[0]
+    if A.shape != (r, K) or B.shape != (N, r):
+        raise ValueError("lora_term: shapes must be x [M, K], A [r, K], B [N, r]")
+    pm, pn = _pairs(M, N, pairs)
+    y = np.zeros(pm.shape[0], dtype=np.float64)
+    tau = np.zeros(pm.shape[0], dtype=np.float64)
+    rc = _load().oracle_lora_term(_ptr(x), _ptr(A), _ptr(B), r, K, _ptr(pm), _ptr(pn), pm.shape[0], _ptr(y),
+                                  _ptr(tau), _threads(threads))
+    if rc != 0:
+        raise ValueError("oracle_lora_term: bad shape")
     return y, tau
 
 

@@ -285,3 +285,40 @@ int oracle_dot_w4a4(const uint8_t* a_codes, const uint8_t* a_scales, float sga,
     }
     return 0;
 }
+
+/* Low-rank branch of a fused LoRA layer [P3 sec.3: y = W_4bit x + B (A x),
+ * the second term in 16 bits with rank r in the tens, added to the quantized
+ * product before the layer returns].  x [M, K], A [r, K], B [N, r] hold the
+ * 16-bit (bf16) values widened to fp32.  For each requested (m, n):
+ *   L*_j = sum_k x[m,k] A[j,k] (fp64),  y*_L = sum_j L*_j B[n,j] (fp64),
+ *   tau_L = 2^-8 sum_j |L*_j| |B[n,j]| + 1e-5 sum_j (sum_k |x[m,k] A[j,k]|) |B[n,j]|
+ * (reading R12: L is held in bf16 between the two products -- one rounding,
+ * at most 2^-8 relative -- and the 1e-5 term is the product tolerance of R9
+ * applied to the down-projection sums). */
+int oracle_lora_term(const float* x, const float* A, const float* B, int64_t r, int64_t K,
+                     const int64_t* pm, const int64_t* pn, int64_t npairs,
+                     double* y, double* tau, int threads) {
+    if (r <= 0 || K <= 0) return -1;
+    #pragma omp parallel for schedule(static) num_threads(threads > 0 ? threads : 1)
+    for (int64_t p = 0; p < npairs; ++p) {
+        const float* xr = x + pm[p] * K;
+        const float* br = B + pn[p] * r;
+        double s = 0.0, t = 0.0;
+        for (int64_t j = 0; j < r; ++j) {
+            const float* ar = A + j * K;
+            double l = 0.0, la = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double v = (double)xr[k] * (double)ar[k];
+                l = l + v;
+                la = la + fabs(v);
+            }
+            double b = (double)br[j];
+            s = s + l * b;
+            t = t + ldexp(fabs(l) * fabs(b), -8) + 1e-5 * la * fabs(b);
+        }
+        y[p] = s;
+        tau[p] = t;
+    }
+    return 0;
+}
+

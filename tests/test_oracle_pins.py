@@ -338,6 +338,33 @@ def test_dot_products_small_integer_exact_and_numpy_crosscheck():
     assert np.all(tau > 0)
 
 
+def test_lora_term_numpy_crosscheck_and_tolerance_parts():
+    rng = np.random.default_rng(11)
+    M, K, r, N = 5, 96, 16, 7
+    x = inputs.bf16_bits_to_f32(inputs.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32)))
+    A = inputs.bf16_bits_to_f32(inputs.to_bf16_bits((rng.standard_normal((r, K)) * 0.05).astype(np.float32)))
+    B = inputs.bf16_bits_to_f32(inputs.to_bf16_bits((rng.standard_normal((N, r)) * 0.05).astype(np.float32)))
+    y, tau = oracle.lora_term(x, A, B)
+    L = x.astype(np.float64) @ A.astype(np.float64).T
+    ref = (L @ B.astype(np.float64).T).reshape(-1)
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-14)
+    S = np.abs(x.astype(np.float64)) @ np.abs(A.astype(np.float64)).T
+    tref = (np.ldexp(np.abs(L), -8) @ np.abs(B.astype(np.float64)).T + 1e-5 * (S @ np.abs(B.astype(np.float64)).T))
+    assert np.allclose(tau, tref.reshape(-1), rtol=1e-12)
+
+
+def test_lora_term_small_integers_exact_and_zero_branch():
+    rng = np.random.default_rng(12)
+    x = rng.integers(-4, 5, size=(3, 32)).astype(np.float32)
+    A = rng.integers(-3, 4, size=(16, 32)).astype(np.float32)
+    B = rng.integers(-2, 3, size=(4, 16)).astype(np.float32)
+    y, _ = oracle.lora_term(x, A, B)
+    exact_int = (x.astype(np.int64) @ A.astype(np.int64).T) @ B.astype(np.int64).T
+    assert np.array_equal(y, exact_int.reshape(-1).astype(np.float64))
+    y0, t0 = oracle.lora_term(x, np.zeros_like(A), B)
+    assert not y0.any() and not t0.any()
+
+
 def test_tiny_config_end_to_end_is_consistent():
     w, xb = inputs.tiny()
     codes, scales, sg = oracle.quantize(w)
