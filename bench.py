@@ -13,7 +13,10 @@ HBM:
             against gate and up [14336, 4096] (gate quantizes A, up reuses it);
             a Flux-like double-stream DiT block: image M = 4096 and text
             M = 512 tokens, to_q/k/v 3072x3072 (k, v reuse q's activation),
-            MLP up 12288x3072 and down 3072x12288.
+            MLP up 12288x3072 and down 3072x12288;
+  lora      the same block with a fused rank-32 low-rank branch on q/k/v
+            (one 9216x3072 layer), MLP up and MLP down (reported per stage,
+            outside value).
 Every stage is launched eagerly on torch's current stream (the stream the
 library launches on) between two HIP events; before each stage a short GPU
 spin kernel holds the queue so the host has enqueued the whole stage before
@@ -43,8 +46,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-peaks", action="store_true", help="skip the measured copy and bf16 GEMM reference rates")
-    p.add_argument("--phases", default="quantize,gemv,gemm",
-                   help="comma list of quantize, gemv, gemm (= prefill + dit), prefill, dit")
+    p.add_argument("--phases", default="quantize,gemv,gemm,lora",
+                   help="comma list of quantize, gemv, gemm (= prefill + dit), prefill, dit, lora "
+                        "(the DiT block with a fused rank-32 LoRA; reported, not part of value)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="only run a plain device-to-device copy of BYTES (HBM counter calibration) and exit")
     return p.parse_args()
@@ -265,6 +269,38 @@ def main():
                 nv.gemm_w4a4(hd, *w["mlp_down"], workspace=ws_h, out=outs["mlp_down"])
 
         capture("gemm_dit_block", dit_block, flops=dit_flops)
+
+    if "lora" in phases:
+        # The same block with a rank-32 low-rank branch fused into every
+        # product: q/k/v as one [9216, 3072] layer sharing one branch, MLP up
+        # and down each with their own; every call quantizes its input and
+        # computes L = x down^T in the same pass.
+        log("[setup] dit block with LoRA")
+        a_img, a_txt, h_img, h_txt = inputs.dit_activations()
+        lora_calls = []
+        lora_flops = 0.0
+        for stream_id, (aa, hh) in enumerate(((a_img, h_img), (a_txt, h_txt))):
+            ad, hd = bf16(aa), bf16(hh)
+            Ms = aa.shape[0]
+            raw = dict(inputs.dit_weights(stream_id))
+            layers = [("qkv", np.concatenate([raw["to_q"], raw["to_k"], raw["to_v"]]), ad),
+                      ("mlp_up", raw["mlp_up"], ad), ("mlp_down", raw["mlp_down"], hd)]
+            del raw
+            for li, (name, wf, act) in enumerate(layers):
+                N, K = wf.shape
+                wq = nv.quantize_mse(f32(wf))
+                down, up = (bf16(t) for t in inputs.lora_factors(32, K, N, 300 + 10 * stream_id + li))
+                wsl = torch.empty(nv.workspace_bytes(nv.OP_GEMM_W4A4_LORA, Ms, K), dtype=torch.uint8, device=dev)
+                out = torch.empty((Ms, N), dtype=torch.bfloat16, device=dev)
+                lora_calls.append((act, wq, down, up, wsl, out))
+                lora_flops += 2.0 * Ms * N * K + 2.0 * Ms * 32 * (K + N)
+            del layers
+
+        def dit_block_lora():
+            for act, wq, down, up, wsl, out in lora_calls:
+                nv.gemm_w4a4(act, *wq, workspace=wsl, out=out, lora=(down, up))
+
+        capture("lora_dit_block", dit_block_lora, flops=lora_flops)
 
     torch.cuda.synchronize()
     log(f"[setup] done in {time.time() - t0:.1f}s; stages: {list(stages)}")

@@ -76,6 +76,111 @@ hipError_t launch_act_quant_f16(const uint16_t* a, int64_t n_elems, const float*
   return hipGetLastError();
 }
 
+// Activation quantization fused with the down projection of a low-rank
+// (LoRA) branch ("NVFP4 en difusion ...", section 3: the layer computes
+// W_4bit x + B (A x), the low-rank term in 16 bits, inside the pass that
+// quantizes the activation so x is read once).  A workgroup owns 16 rows;
+// its 4 waves split K into 32-wide chunks.  Lane (row, g) loads the 8 bf16
+// values x[row][32c + 8g, +8): half of a 16-element block (lanes g and g^1
+// share it), quantized exactly as act_quant_f16_kernel does, and also the A
+// operand of v_mfma_f32_16x16x32_bf16 against lora_down (B operand: lane
+// (j, g) holds lora_down[j][32c + 8g, +8)).  L = x lora_down^T accumulates
+// in fp32, the 4 waves are added in LDS in wave order, and L is stored as
+// bf16 (RNE) [M, 16 RT].
+template <int RT>
+__global__ __launch_bounds__(256) void act_quant_lora_kernel(const uint16_t* __restrict__ a,
+                                                             const float* __restrict__ sg_ptr,
+                                                             const uint16_t* __restrict__ down, int M, int K,
+                                                             uint16_t* __restrict__ a_hat,
+                                                             uint16_t* __restrict__ lora_l) {
+  constexpr int R = 16 * RT;
+  __shared__ f32x4 red[4][RT][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = lane & 15, g = lane >> 4;
+  const int m0 = blockIdx.x * 16;
+  const int rows = min(16, M - m0);
+  const float sg = *sg_ptr;
+  const float inv_sg = 1.0f / sg;
+  const double six_sg = 6.0 * (double)sg;
+  const __amdgpu_buffer_rsrc_t abuf = make_buf(a + (int64_t)m0 * K, (uint32_t)(rows * K * 2));
+  const __amdgpu_buffer_rsrc_t dbuf = make_buf(down, (uint32_t)(R * K * 2));
+  const int nch = K / 32;
+  const int per = (nch + 3) / 4;
+  const int cbeg = wave * per, cend = min(cbeg + per, nch);
+  f32x4 acc[RT];
+#pragma unroll
+  for (int jt = 0; jt < RT; ++jt) acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c = cbeg; c < cend; ++c) {  // wave-uniform
+    const int k = 32 * c + 8 * g;
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(abuf, (row * K + k) * 2, 0, kBufNT);
+    u32x4 d[RT];
+#pragma unroll
+    for (int jt = 0; jt < RT; ++jt)
+      d[jt] = __builtin_amdgcn_raw_buffer_load_b128(dbuf, ((16 * jt + row) * K + k) * 2, 0, 0);
+    float w[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w[2 * j] = bf16_bits_to_f32(v[j] & 0xFFFFu);
+      w[2 * j + 1] = bf16_bits_to_f32(v[j] >> 16);
+    }
+    float mx = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(w[j]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    const uint32_t sc = e4m3_code_rne((double)mx / six_sg);
+    const float sb = e4m3_to_f32(sc);
+    const uint32_t codes = encode8(w, sb, sg, inv_sg);
+    const _Float16 sbh = (_Float16)sb;
+    const f16x2 s2 = {sbh, sbh};
+    f16x2 q[4];
+    fp4x8_to_f16x2(codes, q);
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = __builtin_bit_cast(uint32_t, q[j] * s2);
+    if (row < rows) *reinterpret_cast<u32x4*>(a_hat + (int64_t)(m0 + row) * K + k) = o;
+#pragma unroll
+    for (int jt = 0; jt < RT; ++jt)
+      acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), __builtin_bit_cast(bf16x8, d[jt]),
+                                                        acc[jt], 0, 0, 0);
+  }
+#pragma unroll
+  for (int jt = 0; jt < RT; ++jt) red[wave][jt][lane] = acc[jt];
+  __syncthreads();
+  if (wave == 0) {
+    // lane (j, g) holds L[rows 4g .. 4g+3][16 jt + j]
+#pragma unroll
+    for (int jt = 0; jt < RT; ++jt) {
+      const f32x4 sum = ((red[0][jt][lane] + red[1][jt][lane]) + red[2][jt][lane]) + red[3][jt][lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * g + i;
+        if (m < rows) lora_l[(int64_t)(m0 + m) * R + 16 * jt + row] = (uint16_t)f32_to_bf16_bits(sum[i]);
+      }
+    }
+  }
+}
+
+hipError_t launch_act_quant_lora(const uint16_t* a, const float* sg, const uint16_t* down, int rank, int64_t M,
+                                 int64_t K, uint16_t* a_hat, uint16_t* lora_l, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  const dim3 grid((unsigned)((M + 15) / 16));
+#define NVFP4_AQL(RT)                                                                                             \
+  hipLaunchKernelGGL((act_quant_lora_kernel<RT>), grid, dim3(256), 0, stream, a, sg, down, (int)M, (int)K, a_hat, \
+                     lora_l)
+  switch (rank / 16) {
+    case 1: NVFP4_AQL(1); break;
+    case 2: NVFP4_AQL(2); break;
+    case 3: NVFP4_AQL(3); break;
+    case 4: NVFP4_AQL(4); break;
+    case 5: NVFP4_AQL(5); break;
+    case 6: NVFP4_AQL(6); break;
+    case 7: NVFP4_AQL(7); break;
+    default: NVFP4_AQL(8); break;
+  }
+#undef NVFP4_AQL
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- GEMM
 
 namespace {
@@ -137,11 +242,14 @@ __device__ __forceinline__ void buffer_to_lds2(__amdgpu_buffer_rsrc_t buf, uint3
 // the block scale); A fragments are read one sub-step ahead of their MFMAs.
 // The loop is unrolled by 3 so the stages (separate LDS arrays) are
 // addressed statically.
-template <int BM, int BN, int WM, int WN>
+// LORA: the epilogue adds L lora_up^T (bf16 L [M, rank] from
+// act_quant_lora_kernel, bf16 lora_up [N, rank]) with
+// v_mfma_f32_32x32x16_bf16 after scaling the product by s_gA s_gW.
+template <int BM, int BN, int WM, int WN, bool LORA>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu((BM / WM) * (BN / WN) >= 128 * 128 ? 1 : 2))) void gemm_w4a4_kernel(
     const uint16_t* __restrict__ a_hat, const float* __restrict__ sga_ptr, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ sgw_ptr, int M, int N, int K, void* __restrict__ y,
-    int bf16_out) {
+    int bf16_out, const uint16_t* __restrict__ lora_l, const uint16_t* __restrict__ lora_up, int rank) {
   constexpr int NT = WM * WN * 64;                       // threads
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;    // 32x32 tiles per wave
   constexpr int A_CHUNKS = BM * BK * 2 / 16;             // 16-byte chunks per A stage
@@ -343,6 +451,33 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu((B
 
   // ---- epilogue: acc[i][t][r] = C[row = 8 (r/4) + 4 g + r%4][col = l32]
   const float alpha = (*sga_ptr) * (*sgw_ptr);
+  if constexpr (LORA) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int t = 0; t < TN; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][t][r] *= alpha;
+    // Rows past M and N read as zero; lane (row, g) feeds k = 16 kk + 8 g + j.
+    const __amdgpu_buffer_rsrc_t lbuf = make_buf(lora_l + (int64_t)m0 * rank, (uint32_t)(min(BM, M - m0) * rank * 2));
+    const __amdgpu_buffer_rsrc_t ubuf = make_buf(lora_up + (int64_t)n0 * rank, (uint32_t)(min(BN, N - n0) * rank * 2));
+    for (int kk = 0; kk < rank; kk += 16) {  // uniform
+      bf16x8 lf[TM], uf[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        lf[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                               lbuf, ((wm * (BM / WM) + 32 * i + l32) * rank + kk + 8 * g) * 2, 0, 0));
+#pragma unroll
+      for (int t = 0; t < TN; ++t)
+        uf[t] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                               ubuf, ((wn * (BN / WN) + 32 * t + l32) * rank + kk + 8 * g) * 2, 0, 0));
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+          acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lf[i], uf[t], acc[i][t], 0, 0, 0);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -353,7 +488,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu((B
       for (int r = 0; r < 16; ++r) {
         const int m = m0 + wm * (BM / WM) + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
         if (m >= M) continue;
-        float v = acc[i][t][r] * alpha;
+        float v = LORA ? acc[i][t][r] : acc[i][t][r] * alpha;
         if (bf16_out)
           reinterpret_cast<uint16_t*>(y)[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_bits(v);
         else
@@ -365,20 +500,24 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu((B
 
 hipError_t launch_gemm_w4a4(const uint16_t* a_hat, const float* sga, const uint8_t* codes, const uint8_t* scales,
                             const float* sgw, int64_t M, int64_t N, int64_t K, void* y, bool bf16_out,
-                            hipStream_t stream) {
+                            const uint16_t* lora_l, const uint16_t* lora_up, int rank, hipStream_t stream) {
   // 256 x 256 tiles (8 waves, 128 x 64 per wave) whenever they cover at least
   // half of the 256 CUs; otherwise 128 x 128 tiles (4 waves) for more
   // parallelism on short activations (measured on the prefill and DiT shapes).
   const int b = bf16_out ? 1 : 0;
   const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+#define NVFP4_GEMM(BM, BN, WM, WN, L, T)                                                                       \
+  hipLaunchKernelGGL((gemm_w4a4_kernel<BM, BN, WM, WN, L>), dim3((unsigned)(T)), dim3(WM * WN * 64), 0, stream, \
+                     a_hat, sga, codes, scales, sgw, (int)M, (int)N, (int)K, y, b, lora_l, lora_up, rank)
   if (t256 >= 128) {
-    hipLaunchKernelGGL((gemm_w4a4_kernel<256, 256, 2, 4>), dim3((unsigned)t256), dim3(512), 0, stream, a_hat, sga,
-                       codes, scales, sgw, (int)M, (int)N, (int)K, y, b);
+    if (rank > 0) NVFP4_GEMM(256, 256, 2, 4, true, t256);
+    else NVFP4_GEMM(256, 256, 2, 4, false, t256);
   } else {
-    const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
-    hipLaunchKernelGGL((gemm_w4a4_kernel<128, 128, 2, 2>), dim3((unsigned)t128), dim3(256), 0, stream, a_hat, sga,
-                       codes, scales, sgw, (int)M, (int)N, (int)K, y, b);
+    if (rank > 0) NVFP4_GEMM(128, 128, 2, 2, true, t128);
+    else NVFP4_GEMM(128, 128, 2, 2, false, t128);
   }
+#undef NVFP4_GEMM
   return hipGetLastError();
 }
 

@@ -11,7 +11,7 @@ namespace {
 
 using namespace nvfp4;
 
-constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 2 * 100 + 0;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -70,6 +70,61 @@ size_t gemm_ws_bytes(int64_t M, int64_t K) {
   return 256 + round256((size_t)M * K * 2) + amax_ws_bytes(M * K, true);
 }
 
+// The low-rank variant keeps L = x lora_down^T (bf16 [M, rank <= 128]) right
+// after the quantized activation and moves the amax partials behind it.
+constexpr int kMaxLoraRank = 128;
+
+size_t gemm_lora_ws_bytes(int64_t M, int64_t K) {
+  return gemm_ws_bytes(M, K) + round256((size_t)M * kMaxLoraRank * 2);
+}
+
+int gemm_common(const void* a, const float* a_global, const uint8_t* w_codes, const uint8_t* w_scales,
+                const float* w_global, const void* lora_down, const void* lora_up, int rank, int64_t M, int64_t N,
+                int64_t K, void* y, int y_dtype, int flags, void* workspace, size_t ws_bytes, void* stream) {
+  const bool reuse = (flags & NVFP4_GEMM_REUSE_ACT) != 0;
+  const bool lora = rank != 0;
+  if ((!a && !reuse) || !w_codes || !w_scales || !w_global || !y || !workspace) return NVFP4_ERR_NULL;
+  if (lora && ((!lora_down && !reuse) || !lora_up)) return NVFP4_ERR_NULL;
+  if (flags & ~1) return NVFP4_ERR_FLAGS;
+  if (y_dtype != NVFP4_F32 && y_dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 0 || rank < 0 || !mul_ok(M, K) || !mul_ok(N, K) || !mul_ok(M, N)) return NVFP4_ERR_SHAPE;
+  if (K % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (K % 64 != 0 || K == 0 || M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > (int64_t)1 << 30)
+    return NVFP4_ERR_UNSUPPORTED;
+  if (lora && (rank % 16 != 0 || rank > kMaxLoraRank || K > (int64_t)1 << 22)) return NVFP4_ERR_UNSUPPORTED;
+  if ((!reuse && !aligned(a, 16)) || !aligned(w_codes, 16) || !aligned(w_scales, 4) || !aligned(w_global, 4) ||
+      (a_global && !aligned(a_global, 4)) || !aligned(y, 16) || !aligned(workspace, 256))
+    return NVFP4_ERR_ALIGN;
+  if (lora && ((!reuse && !aligned(lora_down, 16)) || !aligned(lora_up, 16))) return NVFP4_ERR_ALIGN;
+  if (ws_bytes < (lora ? gemm_lora_ws_bytes(M, K) : gemm_ws_bytes(M, K))) return NVFP4_ERR_WORKSPACE;
+  if (M == 0 || N == 0) return NVFP4_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  float* sga = reinterpret_cast<float*>(ws);
+  uint16_t* a_hat = reinterpret_cast<uint16_t*>(ws + 256);
+  const size_t after_a = 256 + round256((size_t)M * K * 2);
+  uint16_t* lora_l = reinterpret_cast<uint16_t*>(ws + after_a);
+  float* partials = reinterpret_cast<float*>(ws + after_a + (lora ? round256((size_t)M * kMaxLoraRank * 2) : 0));
+  clear_error();
+  if (!reuse) {
+    hipError_t e = hipSuccess;
+    if (a_global) {
+      e = hipMemcpyAsync(sga, a_global, sizeof(float), hipMemcpyDeviceToDevice, s);
+    } else {
+      e = launch_global_scale(a, true, M * K, partials, sga, s);
+    }
+    if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
+    const uint16_t* ab = reinterpret_cast<const uint16_t*>(a);
+    e = lora ? launch_act_quant_lora(ab, sga, reinterpret_cast<const uint16_t*>(lora_down), rank, M, K, a_hat,
+                                     lora_l, s)
+             : launch_act_quant_f16(ab, M * K, sga, a_hat, s);
+    if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
+  }
+  return launch_status(launch_gemm_w4a4(a_hat, sga, w_codes, w_scales, w_global, M, N, K, y,
+                                        y_dtype == NVFP4_BF16, lora ? lora_l : nullptr,
+                                        reinterpret_cast<const uint16_t*>(lora_up), rank, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -98,6 +153,7 @@ size_t nvfp4_workspace_bytes(int op, int64_t a, int64_t b) {
                                        ? amax_ws_bytes(a * b, false) : amax_ws_bytes(a * b, true);
     case NVFP4_OP_GEMM_W4A4: return gemm_ws_bytes(a, b);
     case NVFP4_OP_GEMV_W4A16: return 0;
+    case NVFP4_OP_GEMM_W4A4_LORA: return gemm_lora_ws_bytes(a, b);
     default: return 0;
   }
 }
@@ -157,38 +213,18 @@ int nvfp4_gemv_w4a16(const void* x, const uint8_t* w_codes, const uint8_t* w_sca
 int nvfp4_gemm_w4a4(const void* a, const float* a_global, const uint8_t* w_codes, const uint8_t* w_scales,
                     const float* w_global, int64_t M, int64_t N, int64_t K, void* y, int y_dtype, int flags,
                     void* workspace, size_t ws_bytes, void* stream) {
-  const bool reuse = (flags & NVFP4_GEMM_REUSE_ACT) != 0;
-  if ((!a && !reuse) || !w_codes || !w_scales || !w_global || !y || !workspace) return NVFP4_ERR_NULL;
-  if (flags & ~1) return NVFP4_ERR_FLAGS;
-  if (y_dtype != NVFP4_F32 && y_dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
-  if (M < 0 || N < 0 || K < 0 || !mul_ok(M, K) || !mul_ok(N, K) || !mul_ok(M, N)) return NVFP4_ERR_SHAPE;
-  if (K % 16 != 0) return NVFP4_ERR_SHAPE;
-  if (K % 64 != 0 || K == 0 || M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > (int64_t)1 << 30)
-    return NVFP4_ERR_UNSUPPORTED;
-  if ((!reuse && !aligned(a, 16)) || !aligned(w_codes, 16) || !aligned(w_scales, 4) || !aligned(w_global, 4) ||
-      (a_global && !aligned(a_global, 4)) || !aligned(y, 16) || !aligned(workspace, 256))
-    return NVFP4_ERR_ALIGN;
-  if (ws_bytes < gemm_ws_bytes(M, K)) return NVFP4_ERR_WORKSPACE;
-  if (M == 0 || N == 0) return NVFP4_OK;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  char* ws = reinterpret_cast<char*>(workspace);
-  float* sga = reinterpret_cast<float*>(ws);
-  uint16_t* a_hat = reinterpret_cast<uint16_t*>(ws + 256);
-  float* partials = reinterpret_cast<float*>(ws + 256 + round256((size_t)M * K * 2));
-  clear_error();
-  if (!reuse) {
-    hipError_t e = hipSuccess;
-    if (a_global) {
-      e = hipMemcpyAsync(sga, a_global, sizeof(float), hipMemcpyDeviceToDevice, s);
-    } else {
-      e = launch_global_scale(a, true, M * K, partials, sga, s);
-    }
-    if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
-    e = launch_act_quant_f16(reinterpret_cast<const uint16_t*>(a), M * K, sga, a_hat, s);
-    if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
-  }
-  return launch_status(
-      launch_gemm_w4a4(a_hat, sga, w_codes, w_scales, w_global, M, N, K, y, y_dtype == NVFP4_BF16, s));
+  return gemm_common(a, a_global, w_codes, w_scales, w_global, nullptr, nullptr, 0, M, N, K, y, y_dtype, flags,
+                     workspace, ws_bytes, stream);
+}
+
+int nvfp4_gemm_w4a4_lora(const void* a, const float* a_global, const uint8_t* w_codes, const uint8_t* w_scales,
+                         const float* w_global, const void* lora_down, const void* lora_up, int64_t rank, int64_t M,
+                         int64_t N, int64_t K, void* y, int y_dtype, int flags, void* workspace, size_t ws_bytes,
+                         void* stream) {
+  if (rank <= 0) return NVFP4_ERR_SHAPE;
+  if (rank > kMaxLoraRank) return NVFP4_ERR_UNSUPPORTED;
+  return gemm_common(a, a_global, w_codes, w_scales, w_global, lora_down, lora_up, (int)rank, M, N, K, y, y_dtype,
+                     flags, workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -17,6 +17,9 @@ checkpoints and calibration data that are not available):
   dit       Flux-like double-stream block, hidden 3072, MLP 12288, image M = 4096,
             text M = 512; weights t(5) * 0.02 seeds 30..39; activations N(0, 1)
             with 1 % x20 outlier columns, seeds 40..43
+  lora      low-rank factors of rank r (tens): down [r, K] ~ N(0, 1/K),
+            up [N, r] ~ N(0, 0.03^2), bf16; a trained correction of about a
+            tenth of the layer output at r = 32
 """
 import numpy as np
 
@@ -115,3 +118,10 @@ def dit_activations():
         a, _ = with_outlier_columns(a, max(1, k // 100), seed + 100)
         out.append(to_bf16_bits(a))
     return tuple(out)
+
+
+def lora_factors(r, K, N, seed, up_std=0.03):
+    """(down [r, K], up [N, r]) bf16 bits of a rank-r LoRA branch."""
+    down = normal_f32((r, K), seed, std=1.0 / np.sqrt(K))
+    up = normal_f32((N, r), seed + 1, std=up_std)
+    return to_bf16_bits(down), to_bf16_bits(up)

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_LAUNCH, ERR_FLAGS = range(9)
 F32, BF16 = 0, 1
 GLOBAL_COMPUTE, GLOBAL_GIVEN = 0, 1
-OP_QUANTIZE, OP_GEMM_W4A4, OP_GEMV_W4A16 = 0, 1, 2
+OP_QUANTIZE, OP_GEMM_W4A4, OP_GEMV_W4A16, OP_GEMM_W4A4_LORA = 0, 1, 2, 3
 GEMM_QUANTIZE_ACT, GEMM_REUSE_ACT = 0, 1
 
 # name -> (restype, argtypes); mirrors include/nvfp4.h
@@ -28,6 +28,7 @@ SIGNATURES = {
     "nvfp4_dequant": (_I, [_P, _P, _P, _I64, _I64, _P, _I, _P]),
     "nvfp4_gemv_w4a16": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _SZ, _P]),
     "nvfp4_gemm_w4a4": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _I, _P, _SZ, _P]),
+    "nvfp4_gemm_w4a4_lora": (_I, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I, _I, _P, _SZ, _P]),
     "nvfp4_workspace_bytes": (_SZ, [_I, _I64, _I64]),
     "nvfp4_status_string": (ctypes.c_char_p, [_I]),
     "nvfp4_version": (_I, []),
@@ -187,8 +188,11 @@ def gemv_w4a16(x, w_codes, w_scales, w_global, out_dtype=torch.bfloat16, workspa
 
 
 def gemm_w4a4(a, w_codes, w_scales, w_global, a_global=None, out_dtype=torch.bfloat16, workspace=None,
-              out=None, reuse_act=False):
+              out=None, reuse_act=False, lora=None):
     """y = quant(a) W^T with per-call NVFP4 quantization of bf16 a [M, K].
+
+    lora=(down [r, K], up [N, r]) (bf16) adds the 16-bit low-rank term
+    (a down^T) up^T, fused into the same pass (r = 16, 32, ..., 128).
 
     a_global=None computes the activation's tensor scale on the device.
     The workspace (returned contents documented in include/nvfp4.h) may be
@@ -204,14 +208,33 @@ def gemm_w4a4(a, w_codes, w_scales, w_global, a_global=None, out_dtype=torch.bfl
         raise ValueError("reuse_act needs the workspace of the call that quantized the activation")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a.device)
-    ws = workspace if workspace is not None else _alloc_ws(workspace_bytes(OP_GEMM_W4A4, M, K), a.device)
-    st = lib().nvfp4_gemm_w4a4(_ptr(a), _ptr(a_global), _ptr(w_codes), _ptr(w_scales), _ptr(w_global), M, N, K,
-                               _ptr(out), _dtype_code(out.dtype), GEMM_REUSE_ACT if reuse_act else GEMM_QUANTIZE_ACT,
-                               _ptr(ws), 0 if ws is None else ws.numel(), _stream())
-    _check("nvfp4_gemm_w4a4", st)
+    flags = GEMM_REUSE_ACT if reuse_act else GEMM_QUANTIZE_ACT
+    if lora is None:
+        ws = workspace if workspace is not None else _alloc_ws(workspace_bytes(OP_GEMM_W4A4, M, K), a.device)
+        st = lib().nvfp4_gemm_w4a4(_ptr(a), _ptr(a_global), _ptr(w_codes), _ptr(w_scales), _ptr(w_global), M, N, K,
+                                   _ptr(out), _dtype_code(out.dtype), flags, _ptr(ws), ws.numel(), _stream())
+        _check("nvfp4_gemm_w4a4", st)
+        return out
+    down, up = lora
+    _need_cuda(down, up)
+    if down.dtype != torch.bfloat16 or up.dtype != torch.bfloat16 or down.dim() != 2 or up.dim() != 2:
+        raise ValueError("lora = (down [r, K], up [N, r]) must be 2-D bfloat16 tensors")
+    r = down.shape[0]
+    if down.shape != (r, K) or up.shape != (N, r) or not down.is_contiguous() or not up.is_contiguous():
+        raise ValueError("lora = (down [r, K], up [N, r]) must be contiguous with matching sizes")
+    ws = workspace if workspace is not None else _alloc_ws(workspace_bytes(OP_GEMM_W4A4_LORA, M, K), a.device)
+    st = lib().nvfp4_gemm_w4a4_lora(_ptr(a), _ptr(a_global), _ptr(w_codes), _ptr(w_scales), _ptr(w_global),
+                                    _ptr(down), _ptr(up), r, M, N, K, _ptr(out), _dtype_code(out.dtype), flags,
+                                    _ptr(ws), ws.numel(), _stream())
+    _check("nvfp4_gemm_w4a4_lora", st)
     return out
 
 
 def gemm_workspace_layout(M, K):
     """Byte offsets inside the W4A4 workspace: (s_gA, quantized activation fp16 [M, K])."""
     return 0, 256
+
+
+def gemm_lora_l_offset(M, K):
+    """Byte offset of the bf16 low-rank activation L [M, r] in the workspace of the fused LoRA product."""
+    return 256 + (2 * M * K + 255) // 256 * 256

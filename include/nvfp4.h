@@ -74,7 +74,12 @@ enum { NVFP4_GLOBAL_COMPUTE = 0, NVFP4_GLOBAL_GIVEN = 1 };
 enum { NVFP4_GEMM_QUANTIZE_ACT = 0, NVFP4_GEMM_REUSE_ACT = 1 };
 
 /* operation ids for nvfp4_workspace_bytes */
-enum { NVFP4_OP_QUANTIZE = 0, NVFP4_OP_GEMM_W4A4 = 1, NVFP4_OP_GEMV_W4A16 = 2 };
+enum {
+  NVFP4_OP_QUANTIZE = 0,
+  NVFP4_OP_GEMM_W4A4 = 1,
+  NVFP4_OP_GEMV_W4A16 = 2,
+  NVFP4_OP_GEMM_W4A4_LORA = 3
+};
 
 /*
  * nvfp4_quantize_absmax -- NVFP4 encoding with absmax block scales.
@@ -191,9 +196,42 @@ int nvfp4_gemm_w4a4(const void* a, const float* a_global, const uint8_t* w_codes
                     int64_t M, int64_t N, int64_t K, void* y, int y_dtype, int flags,
                     void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * nvfp4_gemm_w4a4_lora -- the W4A4 product plus a 16-bit low-rank branch,
+ * y = A^ W^^T + (A lora_down^T) lora_up^T ("NVFP4 en difusion ...",
+ * section 3: a LoRA cannot be merged into weights already rounded to 4 bits,
+ * so the layer evaluates W_4bit x + B (A x) at run time, the low-rank term
+ * in 16 bits, in the same pass that quantizes the activation).
+ *   a, a_global, w_codes, w_scales, w_global, M, N, K, y, y_dtype:
+ *            as nvfp4_gemm_w4a4 (the low-rank term reads the bf16 `a`, not
+ *            its quantized copy)
+ *   lora_down [rank, K] bf16 (the LoRA "A"), 16-byte aligned
+ *   lora_up   [N, rank] bf16 (the LoRA "B"; fold any LoRA scale into it),
+ *            16-byte aligned
+ *   rank     16, 32, ..., 128 (NVFP4_ERR_UNSUPPORTED otherwise, and for
+ *            K > 2^22; rank <= 0 is NVFP4_ERR_SHAPE)
+ *   workspace >= nvfp4_workspace_bytes(NVFP4_OP_GEMM_W4A4_LORA, M, K)
+ *            bytes, 256-byte aligned, laid out as nvfp4_gemm_w4a4's, with
+ *            L = bf16(A lora_down^T) [M, rank] (row stride rank) starting
+ *            at byte 256 + round_up(2 M K, 256)
+ *   flags    NVFP4_GEMM_REUSE_ACT reuses both the quantized activation and
+ *            L: it needs an earlier call of this function on the same
+ *            workspace with the same a, a_global, lora_down and rank
+ *            (lora_down is then not read)
+ *   L[m, j] = bf16(sum_k a[m,k] lora_down[j,k]), fp32 accumulation;
+ *   y[m, n] = round(fp32(s_gA s_gW) * P[m, n] + sum_j L[m,j] lora_up[n,j])
+ *   with P the W4A4 sum above and the low-rank sum accumulated in fp32
+ *   onto the scaled product.
+ */
+int nvfp4_gemm_w4a4_lora(const void* a, const float* a_global, const uint8_t* w_codes,
+                         const uint8_t* w_scales, const float* w_global,
+                         const void* lora_down, const void* lora_up, int64_t rank,
+                         int64_t M, int64_t N, int64_t K, void* y, int y_dtype, int flags,
+                         void* workspace, size_t ws_bytes, void* stream);
+
 /* Workspace size in bytes for an operation: NVFP4_OP_QUANTIZE with
- * (rows, cols), NVFP4_OP_GEMM_W4A4 with (M, K), NVFP4_OP_GEMV_W4A16 with
- * (M, N); 0 for an unknown op or negative sizes. */
+ * (rows, cols), NVFP4_OP_GEMM_W4A4 and NVFP4_OP_GEMM_W4A4_LORA with (M, K),
+ * NVFP4_OP_GEMV_W4A16 with (M, N); 0 for an unknown op or negative sizes. */
 size_t nvfp4_workspace_bytes(int op, int64_t rows_or_m, int64_t cols_or_k);
 
 /* Static, NUL-terminated description of a status code. */

@@ -25,14 +25,14 @@ def header_functions():
 def test_library_exports_every_declared_symbol():
     L = nv.lib()
     names = header_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(L, n), n
         assert n in nv.SIGNATURES, n
 
 
 def test_status_strings_and_version():
-    assert nv.lib().nvfp4_version() == 10100
+    assert nv.lib().nvfp4_version() == 10200
     for s in range(9):
         assert nv.status_string(s) and nv.status_string(s) != "unknown status"
     assert nv.status_string(99) == "unknown status"
@@ -43,6 +43,9 @@ def test_workspace_sizes():
     g = nv.workspace_bytes(nv.OP_GEMM_W4A4, 4096, 4096)
     assert g >= 256 + 2 * 4096 * 4096
     assert nv.workspace_bytes(nv.OP_GEMV_W4A16, 16, 4096) == 0
+    # the low-rank variant adds L (bf16 [M, 128] at most) after the quantized activation
+    assert nv.workspace_bytes(nv.OP_GEMM_W4A4_LORA, 4096, 4096) == g + 2 * 4096 * 128
+    assert nv.gemm_lora_l_offset(100, 64) == 256 + 12800
     assert nv.workspace_bytes(99, 1, 1) == 0
     assert nv.workspace_bytes(nv.OP_QUANTIZE, -1, 16) == 0
 
@@ -105,6 +108,32 @@ def test_gemm_validation():
     assert f(A16, None, A16, A16, A4, 64, 64, 64, A16, nv.BF16, Q, A16, 16, None) == nv.ERR_WORKSPACE
     assert f(A16, None, A16, A16, A4, 0, 64, 64, A16, nv.BF16, Q, A16, W, None) == nv.OK
     assert f(None, None, A16, A16, A4, 0, 64, 64, A16, nv.BF16, R, A16, W, None) == nv.OK  # reuse: a unused
+
+
+def test_gemm_lora_validation():
+    L = nv.lib()
+    f = L.nvfp4_gemm_w4a4_lora
+    W = 1 << 30
+    Q, R = nv.GEMM_QUANTIZE_ACT, nv.GEMM_REUSE_ACT
+
+    def call(a=A16, down=A16, up=A16, rank=32, M=64, N=64, K=64, flags=Q, ws=A16, wsb=W):
+        return f(a, None, A16, A16, A4, down, up, rank, M, N, K, A16, nv.BF16, flags, ws, wsb, None)
+
+    assert call(down=None) == nv.ERR_NULL
+    assert call(up=None) == nv.ERR_NULL
+    assert call(down=None, up=A16, flags=R, M=0) == nv.OK        # reuse: lora_down unused
+    assert call(rank=0) == nv.ERR_SHAPE
+    assert call(rank=-16) == nv.ERR_SHAPE
+    assert call(rank=8) == nv.ERR_UNSUPPORTED
+    assert call(rank=136) == nv.ERR_UNSUPPORTED
+    assert call(rank=144) == nv.ERR_UNSUPPORTED
+    assert call(K=(1 << 22) + 64) == nv.ERR_UNSUPPORTED
+    assert call(down=A16 + 8) == nv.ERR_ALIGN
+    assert call(up=A16 + 8) == nv.ERR_ALIGN
+    assert call(K=96) == nv.ERR_UNSUPPORTED
+    # the plain product's workspace is too small once L is added
+    assert call(wsb=nv.workspace_bytes(nv.OP_GEMM_W4A4, 64, 64)) == nv.ERR_WORKSPACE
+    assert call(M=0) == nv.OK
 
 
 def test_python_layer_rejects_mismatched_packed_shapes():
