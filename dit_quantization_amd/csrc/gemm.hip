@@ -79,25 +79,35 @@ hipError_t launch_act_quant_f16(const uint16_t* a, int64_t n_elems, const float*
 // Activation quantization fused with the down projection of a low-rank
 // (LoRA) branch ("NVFP4 en difusion ...", section 3: the layer computes
 // W_4bit x + B (A x), the low-rank term in 16 bits, inside the pass that
-// quantizes the activation so x is read once).  A workgroup owns 16 rows;
-// its 4 waves split K into 32-wide chunks.  Lane (row, g) loads the 8 bf16
-// values x[row][32c + 8g, +8): half of a 16-element block (lanes g and g^1
-// share it), quantized exactly as act_quant_f16_kernel does, and also the A
-// operand of v_mfma_f32_16x16x32_bf16 against lora_down (B operand: lane
-// (j, g) holds lora_down[j][32c + 8g, +8)).  L = x lora_down^T accumulates
-// in fp32, the 4 waves are added in LDS in wave order, and L is stored as
-// bf16 (RNE) [M, 16 RT].
+// quantizes the activation so x is read once).
+//
+// A workgroup owns 16 rows and one of `splits` equal ranges of 32-wide K
+// chunks (splits > 1 only when there are too few 16-row tiles to fill the
+// chip); its 4 waves take the range's chunks round-robin, U chunks per
+// batch with every load of the batch in flight before any use.  Lane
+// (row, g) loads the 8 bf16 values x[row][32c + 8g, +8): half of a
+// 16-element block (lanes g and g^1 share it), quantized exactly as
+// act_quant_f16_kernel does, and also the A operand of
+// v_mfma_f32_16x16x32_bf16 against lora_down (B operand: lane (j, g) holds
+// lora_down[j][32c + 8g, +8)).  Chunks past the range load as zero and add
+// nothing.  The 4 waves' fp32 sums are added in LDS in wave order; with one
+// split the result is stored as bf16 (RNE) L [M, 16 RT], otherwise as fp32
+// partial sums [splits, M, 16 RT] that lora_reduce_kernel adds in split
+// order.
 template <int RT>
 __global__ __launch_bounds__(256) void act_quant_lora_kernel(const uint16_t* __restrict__ a,
                                                              const float* __restrict__ sg_ptr,
                                                              const uint16_t* __restrict__ down, int M, int K,
-                                                             uint16_t* __restrict__ a_hat,
-                                                             uint16_t* __restrict__ lora_l) {
+                                                             int splits, int cps, uint16_t* __restrict__ a_hat,
+                                                             uint16_t* __restrict__ lora_l,
+                                                             float* __restrict__ partial) {
   constexpr int R = 16 * RT;
+  constexpr int U = RT <= 3 ? 4 : 2;
   __shared__ f32x4 red[4][RT][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, g = lane >> 4;
-  const int m0 = blockIdx.x * 16;
+  const int tile = blockIdx.x / splits, split = blockIdx.x % splits;
+  const int m0 = tile * 16;
   const int rows = min(16, M - m0);
   const float sg = *sg_ptr;
   const float inv_sg = 1.0f / sg;
@@ -105,43 +115,52 @@ __global__ __launch_bounds__(256) void act_quant_lora_kernel(const uint16_t* __r
   const __amdgpu_buffer_rsrc_t abuf = make_buf(a + (int64_t)m0 * K, (uint32_t)(rows * K * 2));
   const __amdgpu_buffer_rsrc_t dbuf = make_buf(down, (uint32_t)(R * K * 2));
   const int nch = K / 32;
-  const int per = (nch + 3) / 4;
-  const int cbeg = wave * per, cend = min(cbeg + per, nch);
+  const int cbeg = split * cps, cend = min(cbeg + cps, nch);
   f32x4 acc[RT];
 #pragma unroll
   for (int jt = 0; jt < RT; ++jt) acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int c = cbeg; c < cend; ++c) {  // wave-uniform
-    const int k = 32 * c + 8 * g;
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(abuf, (row * K + k) * 2, 0, kBufNT);
-    u32x4 d[RT];
+  for (int c0 = cbeg + wave; c0 < cend; c0 += 4 * U) {  // wave-uniform
+    u32x4 v[U], d[U][RT];
 #pragma unroll
-    for (int jt = 0; jt < RT; ++jt)
-      d[jt] = __builtin_amdgcn_raw_buffer_load_b128(dbuf, ((16 * jt + row) * K + k) * 2, 0, 0);
-    float w[8];
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + 4 * u;
+      const int k = 32 * c + 8 * g;
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(abuf, c < cend ? (row * K + k) * 2 : kBufOOB, 0, kBufNT);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      w[2 * j] = bf16_bits_to_f32(v[j] & 0xFFFFu);
-      w[2 * j + 1] = bf16_bits_to_f32(v[j] >> 16);
+      for (int jt = 0; jt < RT; ++jt)
+        d[u][jt] = __builtin_amdgcn_raw_buffer_load_b128(dbuf, c < cend ? ((16 * jt + row) * K + k) * 2 : kBufOOB,
+                                                         0, 0);
     }
-    float mx = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(w[j]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    const uint32_t sc = e4m3_code_rne((double)mx / six_sg);
-    const float sb = e4m3_to_f32(sc);
-    const uint32_t codes = encode8(w, sb, sg, inv_sg);
-    const _Float16 sbh = (_Float16)sb;
-    const f16x2 s2 = {sbh, sbh};
-    f16x2 q[4];
-    fp4x8_to_f16x2(codes, q);
-    u32x4 o;
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + 4 * u;
+      const int k = 32 * c + 8 * g;
+      float w[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = __builtin_bit_cast(uint32_t, q[j] * s2);
-    if (row < rows) *reinterpret_cast<u32x4*>(a_hat + (int64_t)(m0 + row) * K + k) = o;
+      for (int j = 0; j < 4; ++j) {
+        w[2 * j] = bf16_bits_to_f32(v[u][j] & 0xFFFFu);
+        w[2 * j + 1] = bf16_bits_to_f32(v[u][j] >> 16);
+      }
+      float mx = 0.0f;
 #pragma unroll
-    for (int jt = 0; jt < RT; ++jt)
-      acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), __builtin_bit_cast(bf16x8, d[jt]),
-                                                        acc[jt], 0, 0, 0);
+      for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(w[j]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      const uint32_t sc = e4m3_code_rne((double)mx / six_sg);
+      const float sb = e4m3_to_f32(sc);
+      const uint32_t codes = encode8(w, sb, sg, inv_sg);
+      const _Float16 sbh = (_Float16)sb;
+      const f16x2 s2 = {sbh, sbh};
+      f16x2 q[4];
+      fp4x8_to_f16x2(codes, q);
+      u32x4 o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = __builtin_bit_cast(uint32_t, q[j] * s2);
+      if (row < rows && c < cend) *reinterpret_cast<u32x4*>(a_hat + (int64_t)(m0 + row) * K + k) = o;
+#pragma unroll
+      for (int jt = 0; jt < RT; ++jt)
+        acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v[u]),
+                                                          __builtin_bit_cast(bf16x8, d[u][jt]), acc[jt], 0, 0, 0);
+    }
   }
 #pragma unroll
   for (int jt = 0; jt < RT; ++jt) red[wave][jt][lane] = acc[jt];
@@ -154,19 +173,48 @@ __global__ __launch_bounds__(256) void act_quant_lora_kernel(const uint16_t* __r
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = 4 * g + i;
-        if (m < rows) lora_l[(int64_t)(m0 + m) * R + 16 * jt + row] = (uint16_t)f32_to_bf16_bits(sum[i]);
+        if (m >= rows) continue;
+        const int64_t at = (int64_t)(m0 + m) * R + 16 * jt + row;
+        if (splits == 1) lora_l[at] = (uint16_t)f32_to_bf16_bits(sum[i]);
+        else partial[(int64_t)split * M * R + at] = sum[i];
       }
     }
   }
 }
 
+// L[i] = bf16(((p[0][i] + p[1][i]) + ...) + p[splits-1][i]) over the n = M R
+// entries of the split partial sums.
+__global__ __launch_bounds__(256) void lora_reduce_kernel(const float* __restrict__ partial, int splits, int64_t n,
+                                                          uint16_t* __restrict__ lora_l) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = partial[i];
+  for (int t = 1; t < splits; ++t) s += partial[t * n + i];
+  lora_l[i] = (uint16_t)f32_to_bf16_bits(s);
+}
+
+int lora_splits(int64_t M, int64_t K) {
+  // Enough (16-row tile, K range) workgroups to give each CU about four,
+  // with at least four chunks (one per wave) in each range.
+  const int64_t tiles = (M + 15) / 16, nch = K / 32;
+  if (tiles == 0 || tiles >= 1024) return 1;
+  int64_t s = (1024 + tiles - 1) / tiles;
+  if (s > nch / 4) s = nch / 4;
+  if (s <= 1) return 1;
+  const int64_t cps = (nch + s - 1) / s;
+  return (int)((nch + cps - 1) / cps);  // no empty range
+}
+
 hipError_t launch_act_quant_lora(const uint16_t* a, const float* sg, const uint16_t* down, int rank, int64_t M,
-                                 int64_t K, uint16_t* a_hat, uint16_t* lora_l, hipStream_t stream) {
+                                 int64_t K, uint16_t* a_hat, uint16_t* lora_l, float* partial, hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  const dim3 grid((unsigned)((M + 15) / 16));
+  const int splits = lora_splits(M, K);
+  const int nch = (int)(K / 32);
+  const int cps = (nch + splits - 1) / splits;
+  const dim3 grid((unsigned)(((M + 15) / 16) * splits));
 #define NVFP4_AQL(RT)                                                                                             \
-  hipLaunchKernelGGL((act_quant_lora_kernel<RT>), grid, dim3(256), 0, stream, a, sg, down, (int)M, (int)K, a_hat, \
-                     lora_l)
+  hipLaunchKernelGGL((act_quant_lora_kernel<RT>), grid, dim3(256), 0, stream, a, sg, down, (int)M, (int)K, splits, \
+                     cps, a_hat, lora_l, partial)
   switch (rank / 16) {
     case 1: NVFP4_AQL(1); break;
     case 2: NVFP4_AQL(2); break;
@@ -178,6 +226,11 @@ hipError_t launch_act_quant_lora(const uint16_t* a, const float* sg, const uint1
     default: NVFP4_AQL(8); break;
   }
 #undef NVFP4_AQL
+  if (splits > 1) {
+    const int64_t n = M * rank;
+    hipLaunchKernelGGL(lora_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, partial, splits,
+                       n, lora_l);
+  }
   return hipGetLastError();
 }
 

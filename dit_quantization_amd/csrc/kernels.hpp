@@ -22,8 +22,11 @@ hipError_t launch_gemv_w4a16(const uint16_t* x, const uint8_t* codes, const uint
                              int64_t M, int64_t N, int64_t K, void* y, bool bf16_out, hipStream_t stream);
 hipError_t launch_act_quant_f16(const uint16_t* a, int64_t n_elems, const float* sg, uint16_t* a_hat,
                                 hipStream_t stream);
+// K ranges the fused activation-quantization + LoRA-down pass splits each
+// 16-row tile into; splits > 1 needs fp32 partials of splits * M * rank.
+int lora_splits(int64_t M, int64_t K);
 hipError_t launch_act_quant_lora(const uint16_t* a, const float* sg, const uint16_t* down, int rank, int64_t M,
-                                 int64_t K, uint16_t* a_hat, uint16_t* lora_l, hipStream_t stream);
+                                 int64_t K, uint16_t* a_hat, uint16_t* lora_l, float* partial, hipStream_t stream);
 hipError_t launch_gemm_w4a4(const uint16_t* a_hat, const float* sga, const uint8_t* codes, const uint8_t* scales,
                             const float* sgw, int64_t M, int64_t N, int64_t K, void* y, bool bf16_out,
                             const uint16_t* lora_l, const uint16_t* lora_up, int rank, hipStream_t stream);

@@ -74,8 +74,13 @@ size_t gemm_ws_bytes(int64_t M, int64_t K) {
 // after the quantized activation and moves the amax partials behind it.
 constexpr int kMaxLoraRank = 128;
 
+size_t lora_partial_bytes(int64_t M, int64_t K) {
+  const int s = K > 0 ? lora_splits(M, K) : 1;
+  return s > 1 ? round256((size_t)s * M * kMaxLoraRank * 4) : 0;
+}
+
 size_t gemm_lora_ws_bytes(int64_t M, int64_t K) {
-  return gemm_ws_bytes(M, K) + round256((size_t)M * kMaxLoraRank * 2);
+  return gemm_ws_bytes(M, K) + round256((size_t)M * kMaxLoraRank * 2) + lora_partial_bytes(M, K);
 }
 
 int gemm_common(const void* a, const float* a_global, const uint8_t* w_codes, const uint8_t* w_scales,
@@ -104,7 +109,9 @@ int gemm_common(const void* a, const float* a_global, const uint8_t* w_codes, co
   uint16_t* a_hat = reinterpret_cast<uint16_t*>(ws + 256);
   const size_t after_a = 256 + round256((size_t)M * K * 2);
   uint16_t* lora_l = reinterpret_cast<uint16_t*>(ws + after_a);
-  float* partials = reinterpret_cast<float*>(ws + after_a + (lora ? round256((size_t)M * kMaxLoraRank * 2) : 0));
+  const size_t after_l = after_a + (lora ? round256((size_t)M * kMaxLoraRank * 2) : 0);
+  float* lora_partial = reinterpret_cast<float*>(ws + after_l);
+  float* partials = reinterpret_cast<float*>(ws + after_l + (lora ? lora_partial_bytes(M, K) : 0));
   clear_error();
   if (!reuse) {
     hipError_t e = hipSuccess;
@@ -116,7 +123,7 @@ int gemm_common(const void* a, const float* a_global, const uint8_t* w_codes, co
     if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
     const uint16_t* ab = reinterpret_cast<const uint16_t*>(a);
     e = lora ? launch_act_quant_lora(ab, sga, reinterpret_cast<const uint16_t*>(lora_down), rank, M, K, a_hat,
-                                     lora_l, s)
+                                     lora_l, lora_partial, s)
              : launch_act_quant_f16(ab, M * K, sga, a_hat, s);
     if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
   }

@@ -70,8 +70,11 @@ def _check_lora(ab, w, down_b, up_b, pairs=None, a_global=None, what=""):
     assert_within_tau(host(yp)[sel].reshape(-1), ystar - lst, tau - lt, what + " plain")
 
 
+# The down projection splits K over workgroups when there are few 16-row
+# tiles: one range (M = 1, 70, 16400), 4 (M = 300), 32 (M = 257), 8 (M = 33)
+# and 3 uneven ranges of 5, 5, 4 chunks (M = 40, K = 448).
 @pytest.mark.parametrize("mnkr", [(1, 64, 64, 16), (70, 130, 192, 32), (300, 520, 512, 128), (257, 300, 4096, 48),
-                                  (33, 96, 1024, 80)])
+                                  (33, 96, 1024, 80), (40, 200, 448, 16), (16400, 64, 64, 16)])
 def test_lora_ragged_full_compare(mnkr):
     M, N, K, r = mnkr
     a = inputs.normal_f32((M, K), M + 5)
