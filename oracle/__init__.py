@@ -50,6 +50,8 @@ def _load():
     lib.oracle_mse_scale_code.argtypes = [P, ctypes.c_float]
     lib.oracle_lora_term.restype = ctypes.c_int
     lib.oracle_lora_term.argtypes = [P, P, P, i64, i64, P, P, i64, P, P, ctypes.c_int]
+    lib.oracle_act_scale_errors.restype = ctypes.c_int
+    lib.oracle_act_scale_errors.argtypes = [P, i64, ctypes.c_float, P, ctypes.c_int]
     lib.oracle_4o6_scale_code.restype = ctypes.c_int
     lib.oracle_4o6_scale_code.argtypes = [P, ctypes.c_float]
     lib.oracle_block_error.restype = ctypes.c_double
@@ -223,6 +225,40 @@ def lora_term(x, A, B, pairs=None, threads=None):
     if rc != 0:
         raise ValueError("oracle_lora_term: bad shape")
     return y, tau
+
+
+SWEEP_CANDIDATES = 17
+
+
+def act_scale_candidates(amax):
+    """Candidate static activation tensor scales s_c = fp32(amax / (6 v_c)),
+    v_c = E4M3(126 - c) = 448 ... 112 (all 1.0 when amax == 0); reading R13."""
+    lib = _load()
+    if np.float32(amax) == 0:
+        return np.ones(SWEEP_CANDIDATES, dtype=np.float32)
+    return np.array([np.float32(np.float64(np.float32(amax)) / (6.0 * lib.oracle_e4m3_value(126 - c)))
+                     for c in range(SWEEP_CANDIDATES)], dtype=np.float32)
+
+
+def act_scale_sweep(batches, amax=None, threads=None):
+    """FP8 candidate sweep for a static activation tensor scale over calibration
+    batches (each any shape with a multiple of 16 elements per row-major
+    block run).  Returns (errors fp64 [17], best index, chosen scale fp32,
+    amax): errors accumulate over the batches in order, the smallest error
+    wins and ties keep the lower index."""
+    batches = [np.ascontiguousarray(b, dtype=np.float32).reshape(-1) for b in batches]
+    if amax is None:
+        amax = max((float(_load().oracle_amax(_ptr(b), b.size)) for b in batches), default=0.0)
+    amax = np.float32(amax)
+    err = np.zeros(SWEEP_CANDIDATES, dtype=np.float64)
+    for b in batches:
+        if _load().oracle_act_scale_errors(_ptr(b), b.size, amax, _ptr(err), _threads(threads)) != 0:
+            raise ValueError("act_scale_sweep: a batch's size is not a multiple of 16")
+    best = 0
+    for c in range(1, SWEEP_CANDIDATES):
+        if err[c] < err[best]:
+            best = c
+    return err, best, act_scale_candidates(amax)[best], amax
 
 
 def bf16_rne_from_f64(v):

@@ -31,6 +31,7 @@
  *   sequential sum of rounded squares; ties keep the smaller scale.
  *   R11 four-over-six: candidates max/(6 s_g) and max/(4 s_g), each rounded
  *   to E4M3; the R5 error decides, ties keep the smaller scale.
+ *   R13 activation scale sweep: see oracle_act_scale_errors.
  */
 #include <math.h>
 #include <stdint.h>
@@ -322,3 +323,31 @@ int oracle_lora_term(const float* x, const float* A, const float* B, int64_t r, 
     return 0;
 }
 
+/* ---- static activation tensor scale: FP8 candidate sweep --------------- */
+
+/* Errors of the candidate static activation tensor scales over one batch of
+ * calibration activations, added to err[0..16].
+ * [P1 sec.1, "Tres preguntas", question 3: activation scales have to be
+ * calibrated on real activations whose ranges are recorded; P1 sec.2, box
+ * "En tu proyecto": the MSE calibration also sweeps candidate activation
+ * scales in FP8.]  Reading R13: candidate c (0..16) puts the block scale of
+ * the calibration set's largest block on the E4M3 value v_c = E4M3(126 - c),
+ * i.e. 448 down to 112, so s_c = fp32(amax / (6 v_c)) (s_c = 1 for every c
+ * when amax == 0; c = 0 is the dynamic rule's s_g).  A candidate's error is
+ * the sum over every block, in order, of the absmax-quantized block's squared
+ * error (R5 arithmetic) under s_c, accumulated across batches in call order.
+ * n must be a multiple of 16. */
+int oracle_act_scale_errors(const float* x, int64_t n, float amax, double* err, int threads) {
+    if (n % 16 != 0) return -1;
+    #pragma omp parallel for schedule(static) num_threads(threads > 0 ? threads : 1)
+    for (int c = 0; c < 17; ++c) {
+        float s = amax == 0.0f ? 1.0f : (float)((double)amax / (6.0 * oracle_e4m3_value(126 - c)));
+        double e = err[c];
+        for (int64_t b = 0; b < n / 16; ++b) {
+            const float* w = x + 16 * b;
+            e = e + oracle_block_error(w, s, oracle_absmax_scale_code(w, s));
+        }
+        err[c] = e;
+    }
+    return 0;
+}

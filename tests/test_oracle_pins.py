@@ -391,3 +391,77 @@ def test_mse_statistics_report():
     ratio = e4[sm.reshape(-1)] / np.maximum(e4[sa.reshape(-1)], 1e-30)
     print(f"median s_mse/s_absmax = {np.median(ratio):.3f}; noise variance reduction = "
           f"{1 - em.sum() / ea.sum():.3f}; blocks improved = {(bm < ba).mean():.3f}")
+
+
+# ---------------------------------------------------------------- static activation scale sweep (R13)
+
+def _e4m3_from_torch(byte):
+    return float(torch.tensor([byte], dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64)[0])
+
+
+def test_act_scale_candidates_exact():
+    vs = [_e4m3_from_torch(126 - c) for c in range(oracle.SWEEP_CANDIDATES)]
+    assert vs[0] == 448.0 and vs[-1] == 112.0 and all(a > b for a, b in zip(vs, vs[1:]))
+    g = inputs.rng(31)
+    for amax in list(g.uniform(0, 50, 200).astype(np.float32)) + [np.float32(2304.0), np.float32(1e-30)]:
+        cand = oracle.act_scale_candidates(amax)
+        for c, v in enumerate(vs):
+            assert cand[c] == float(exact.fp32(F(float(amax)) / (6 * F(v)))), (amax, c)
+        assert cand[0] == oracle.global_scale(float(amax))      # c = 0 is the dynamic rule's s_g
+    assert np.all(oracle.act_scale_candidates(0.0) == 1.0)
+
+
+def _exact_sweep(batches):
+    amax = max(float(np.abs(b).max()) for b in batches)
+    vs = [F(_e4m3_from_torch(126 - c)) for c in range(oracle.SWEEP_CANDIDATES)]
+    errs = []
+    for v in vs:
+        s = exact.fp32(F(amax) / (6 * v)) if amax > 0 else F(1)
+        e = F(0)
+        for b in batches:
+            for blk in b.reshape(-1, 16):
+                bl = [F(float(t)) for t in blk]
+                e += exact.block_error(bl, exact.absmax_scale(bl, s), s)
+        errs.append(e)
+    return errs
+
+
+def test_act_scale_sweep_matches_exact_rational():
+    b1 = _blocks_tiny(41, 8)
+    b2 = _blocks_tiny(42, 8) * np.float32(3.0)
+    err, best, scale, amax = oracle.act_scale_sweep([b1, b2])
+    want = _exact_sweep([b1, b2])
+    for c in range(oracle.SWEEP_CANDIDATES):
+        assert abs(err[c] - float(want[c])) <= 1e-12 * float(want[c]), c
+    exact_best = min(range(oracle.SWEEP_CANDIDATES), key=lambda c: (want[c], c))
+    assert best == exact_best
+    assert scale == oracle.act_scale_candidates(amax)[best]
+
+
+def test_act_scale_sweep_constructed_winner():
+    """amax = 6 * 384: candidate 2 (v = 384) gives s = 1 exactly, under which
+    both blocks lie on their grids (scales 384 and 1), so its error is exactly
+    zero; the dynamic rule's s_g = fp32(2304 / 2688) rounds and cannot."""
+    blk1 = np.array([2304, -1152, 576, 192, 0, 384, -768, 1536, 1152, -2304, 96 * 2, 0, 576, -192, 384, 768],
+                    dtype=np.float32)
+    blk2 = np.array([6, -3, 1.5, 0.5, 1, -2, 4, 0, -6, 3, 2, -1, 0.5, -0.5, 1.5, 4], dtype=np.float32)
+    err, best, scale, amax = oracle.act_scale_sweep([np.concatenate([blk1, blk2])])
+    assert amax == 2304.0 and best == 2 and scale == 1.0
+    assert err[2] == 0.0 and err[0] > 0 and err[1] > 0
+    want = _exact_sweep([np.concatenate([blk1, blk2])])
+    assert want[2] == 0 and all(want[c] > 0 for c in (0, 1))
+
+
+def test_act_scale_sweep_accumulates_batches_in_order():
+    b1 = _blocks_tiny(43, 12)
+    b2 = _blocks_tiny(44, 12) * np.float32(0.5)
+    e12, best12, _, amax = oracle.act_scale_sweep([b1, b2])
+    ecat, bestcat, _, _ = oracle.act_scale_sweep([np.concatenate([b1.reshape(-1), b2.reshape(-1)])])
+    assert np.array_equal(e12, ecat) and best12 == bestcat
+    e1, _, _, _ = oracle.act_scale_sweep([b1], amax=amax)
+    assert np.all(e1 < e12)                      # the second batch adds its own error
+
+
+def test_act_scale_sweep_zero_input():
+    err, best, scale, amax = oracle.act_scale_sweep([np.zeros((4, 32), dtype=np.float32)])
+    assert amax == 0.0 and best == 0 and scale == 1.0 and np.all(err == 0)
