@@ -16,7 +16,12 @@ HBM:
             MLP up 12288x3072 and down 3072x12288;
   lora      the same block with a fused rank-32 low-rank branch on q/k/v
             (one 9216x3072 layer), MLP up and MLP down (reported per stage,
-            outside value).
+            outside value);
+  calibrate the static activation scale: running amax and the FP8
+            candidate sweep over four 512x3072 batches and the 4096x3072
+            image-stream input, and the prefill gate product with a
+            calibrated scale given (one-pass activation quantization);
+            reported outside value.
 Every stage is launched eagerly on torch's current stream (the stream the
 library launches on) between two HIP events; before each stage a short GPU
 spin kernel holds the queue so the host has enqueued the whole stage before
@@ -46,9 +51,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-peaks", action="store_true", help="skip the measured copy and bf16 GEMM reference rates")
-    p.add_argument("--phases", default="quantize,gemv,gemm,lora",
+    p.add_argument("--phases", default="quantize,gemv,gemm,lora,calibrate",
                    help="comma list of quantize, gemv, gemm (= prefill + dit), prefill, dit, lora "
-                        "(the DiT block with a fused rank-32 LoRA; reported, not part of value)")
+                        "(the DiT block with a fused rank-32 LoRA), calibrate (static activation scale sweep and "
+                        "the prefill gate with that scale); lora and calibrate are reported, not part of value")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="only run a plain device-to-device copy of BYTES (HBM counter calibration) and exit")
     return p.parse_args()
@@ -269,6 +275,51 @@ def main():
                 nv.gemm_w4a4(hd, *w["mlp_down"], workspace=ws_h, out=outs["mlp_down"])
 
         capture("gemm_dit_block", dit_block, flops=dit_flops)
+
+    if "calibrate" in phases:
+        # Static activation scale: running amax + FP8 candidate sweep over
+        # calibration batches (four 512x3072 text-stream batches and the
+        # 4096x3072 image-stream input), then the prefill gate product with
+        # that scale given, whose activation quantization is one pass.
+        log("[setup] calibration batches")
+        cal = []
+        for seed in range(4):
+            x = inputs.normal_f32((512, 3072), 500 + seed)
+            x, _ = inputs.with_outlier_columns(x, 30, 600 + seed)
+            cal.append(bf16(inputs.to_bf16_bits(x)))
+        cal.append(bf16(inputs.dit_activations()[0]))
+        cal_blocks = sum(t.numel() for t in cal) / 16
+        cal_ws = torch.empty(max(nv.workspace_bytes(nv.OP_ACT_CALIBRATE, *t.shape) for t in cal), dtype=torch.uint8,
+                             device=dev)
+        cal_amax = torch.zeros(1, dtype=torch.float32, device=dev)
+        cal_err = torch.zeros(nv.SWEEP_CANDIDATES, dtype=torch.float64, device=dev)
+        cal_scale = torch.empty(1, dtype=torch.float32, device=dev)
+
+        def calibrate():
+            cal_amax.zero_()
+            cal_err.zero_()
+            for t in cal:
+                nv.act_amax(t, cal_amax, workspace=cal_ws)
+            for t in cal:
+                nv.act_scale_sweep(t, cal_amax, cal_err, cal_scale, workspace=cal_ws)
+
+        capture("calibrate_sweep", calibrate, nbytes=cal_blocks * 16 * 2 * 2,
+                ops=cal_blocks * nv.SWEEP_CANDIDATES * 16 * 6.0)
+
+        a_pf = bf16(inputs.prefill_activation())
+        (_, w_gate), = list(inputs.layerset(["gate"]))
+        wq_gate = nv.quantize_mse(f32(w_gate))
+        del w_gate
+        Mp, Kp = a_pf.shape
+        Np = wq_gate[0].shape[0]
+        pf_scale, _, _ = nv.calibrate_act_scale([a_pf])
+        ws_pf = torch.empty(nv.workspace_bytes(nv.OP_GEMM_W4A4, Mp, Kp), dtype=torch.uint8, device=dev)
+        y_pf = torch.empty((Mp, Np), dtype=torch.bfloat16, device=dev)
+
+        def static_gate():
+            nv.gemm_w4a4(a_pf, *wq_gate, a_global=pf_scale, workspace=ws_pf, out=y_pf)
+
+        capture("static_prefill_gate", static_gate, flops=2.0 * Mp * Np * Kp)
 
     if "lora" in phases:
         # The same block with a rank-32 low-rank branch fused into every

@@ -8,10 +8,16 @@
 namespace nvfp4 {
 
 constexpr int kMaxAmaxPartials = 2048;
+constexpr int kSweepCandidates = 17;  // static activation scale candidates, E4M3 448 down to 112
 
 int amax_partial_count(int64_t n_elems, bool bf16);
 hipError_t launch_global_scale(const void* x, bool bf16, int64_t n_elems, float* partials, float* sg_out,
                                hipStream_t stream);
+hipError_t launch_running_amax(const void* x, bool bf16, int64_t n_elems, float* partials, float* amax,
+                               hipStream_t stream);
+int act_sweep_partial_count(int64_t n_elems);
+hipError_t launch_act_scale_sweep(const uint16_t* x, int64_t n_elems, const float* amax, double* partials,
+                                  double* errors, float* scale, hipStream_t stream);
 hipError_t launch_quantize_absmax(const void* x, bool bf16, int64_t n_elems, const float* sg, uint8_t* codes,
                                   uint8_t* scales, hipStream_t stream);
 hipError_t launch_quantize_search(const void* x, bool bf16, bool four_over_six, int64_t n_elems, const float* sg,

@@ -11,7 +11,8 @@ namespace {
 
 using namespace nvfp4;
 
-constexpr int kVersion = 1 * 10000 + 2 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 3 * 100 + 0;
+static_assert(kSweepCandidates == NVFP4_SWEEP_CANDIDATES, "candidate count of the activation scale sweep");
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -81,6 +82,13 @@ size_t lora_partial_bytes(int64_t M, int64_t K) {
 
 size_t gemm_lora_ws_bytes(int64_t M, int64_t K) {
   return gemm_ws_bytes(M, K) + round256((size_t)M * kMaxLoraRank * 2) + lora_partial_bytes(M, K);
+}
+
+size_t calibrate_ws_bytes(int64_t n) {
+  const size_t amax = amax_ws_bytes(n, false) > amax_ws_bytes(n, true) ? amax_ws_bytes(n, false)
+                                                                        : amax_ws_bytes(n, true);
+  const size_t sweep = round256(sizeof(double) * NVFP4_SWEEP_CANDIDATES * (size_t)act_sweep_partial_count(n));
+  return amax > sweep ? amax : sweep;
 }
 
 int gemm_common(const void* a, const float* a_global, const uint8_t* w_codes, const uint8_t* w_scales,
@@ -161,6 +169,7 @@ size_t nvfp4_workspace_bytes(int op, int64_t a, int64_t b) {
     case NVFP4_OP_GEMM_W4A4: return gemm_ws_bytes(a, b);
     case NVFP4_OP_GEMV_W4A16: return 0;
     case NVFP4_OP_GEMM_W4A4_LORA: return gemm_lora_ws_bytes(a, b);
+    case NVFP4_OP_ACT_CALIBRATE: return calibrate_ws_bytes(a * b);
     default: return 0;
   }
 }
@@ -232,6 +241,32 @@ int nvfp4_gemm_w4a4_lora(const void* a, const float* a_global, const uint8_t* w_
   if (rank > kMaxLoraRank) return NVFP4_ERR_UNSUPPORTED;
   return gemm_common(a, a_global, w_codes, w_scales, w_global, lora_down, lora_up, (int)rank, M, N, K, y, y_dtype,
                      flags, workspace, ws_bytes, stream);
+}
+
+int nvfp4_act_amax(const void* x, int x_dtype, int64_t rows, int64_t cols, float* amax, void* workspace,
+                   size_t ws_bytes, void* stream) {
+  if (!x || !amax || !workspace) return NVFP4_ERR_NULL;
+  if (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
+  if (rows < 0 || cols < 0 || !mul_ok(rows, cols) || cols % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(amax, 4)) return NVFP4_ERR_ALIGN;
+  if (ws_bytes < calibrate_ws_bytes(rows * cols)) return NVFP4_ERR_WORKSPACE;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  clear_error();
+  return launch_status(launch_running_amax(x, x_dtype == NVFP4_BF16, rows * cols, reinterpret_cast<float*>(workspace),
+                                           amax, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int nvfp4_act_scale_sweep(const void* x, int64_t rows, int64_t cols, const float* amax, double* errors, float* scale,
+                          void* workspace, size_t ws_bytes, void* stream) {
+  if (!x || !amax || !errors || !scale || !workspace) return NVFP4_ERR_NULL;
+  if (rows < 0 || cols < 0 || !mul_ok(rows, cols) || cols % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(amax, 4) || !aligned(errors, 8) || !aligned(scale, 4) || !aligned(workspace, 256))
+    return NVFP4_ERR_ALIGN;
+  if (ws_bytes < calibrate_ws_bytes(rows * cols)) return NVFP4_ERR_WORKSPACE;
+  clear_error();
+  return launch_status(launch_act_scale_sweep(reinterpret_cast<const uint16_t*>(x), rows * cols, amax,
+                                              reinterpret_cast<double*>(workspace), errors, scale,
+                                              reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -41,15 +41,21 @@ __global__ __launch_bounds__(256) void amax_partial_kernel(const void* __restric
   if (threadIdx.x == 0) partials[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
+// kRunningMax: out = max(out, amax) (a running calibration range) instead of
+// out = s_g(amax).
+template <bool kRunningMax>
 __global__ __launch_bounds__(256) void amax_finalize_kernel(const float* __restrict__ partials, int np,
-                                                            float* __restrict__ sg_out) {
+                                                            float* __restrict__ out) {
   float m = 0.0f;
   for (int i = threadIdx.x; i < np; i += blockDim.x) m = fmaxf(m, partials[i]);
   __shared__ float red[4];
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (threadIdx.x == 0) *sg_out = global_scale_from_amax(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+  if (threadIdx.x == 0) {
+    const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    *out = kRunningMax ? fmaxf(*out, amax) : global_scale_from_amax(amax);
+  }
 }
 
 int amax_partial_count(int64_t n_elems, bool bf16) {
@@ -60,15 +66,28 @@ int amax_partial_count(int64_t n_elems, bool bf16) {
   return (int)wg;
 }
 
-hipError_t launch_global_scale(const void* x, bool bf16, int64_t n_elems, float* partials, float* sg_out,
-                               hipStream_t stream) {
-  int np = amax_partial_count(n_elems, bf16);
+static void launch_amax_partials(const void* x, bool bf16, int64_t n_elems, float* partials, int np,
+                                 hipStream_t stream) {
   int64_t n_vec = n_elems / (bf16 ? 8 : 4);
   if (bf16)
     hipLaunchKernelGGL(amax_partial_kernel<true>, dim3(np), dim3(256), 0, stream, x, n_vec, partials);
   else
     hipLaunchKernelGGL(amax_partial_kernel<false>, dim3(np), dim3(256), 0, stream, x, n_vec, partials);
-  hipLaunchKernelGGL(amax_finalize_kernel, dim3(1), dim3(256), 0, stream, partials, np, sg_out);
+}
+
+hipError_t launch_global_scale(const void* x, bool bf16, int64_t n_elems, float* partials, float* sg_out,
+                               hipStream_t stream) {
+  int np = amax_partial_count(n_elems, bf16);
+  launch_amax_partials(x, bf16, n_elems, partials, np, stream);
+  hipLaunchKernelGGL(amax_finalize_kernel<false>, dim3(1), dim3(256), 0, stream, partials, np, sg_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_running_amax(const void* x, bool bf16, int64_t n_elems, float* partials, float* amax,
+                               hipStream_t stream) {
+  int np = amax_partial_count(n_elems, bf16);
+  launch_amax_partials(x, bf16, n_elems, partials, np, stream);
+  hipLaunchKernelGGL(amax_finalize_kernel<true>, dim3(1), dim3(256), 0, stream, partials, np, amax);
   return hipGetLastError();
 }
 

@@ -22,9 +22,10 @@
 // quotient x = |W| (1 / c) (1 / s_g), whose relative error is below 3 ulps.
 // Every E2M1 rounding midpoint has at most 3 significant bits, so when no
 // x of the block lies within 8 ulps of a number whose low 21 mantissa bits
-// are zero, x and the exact quotient round alike and the fast codes stand;
-// otherwise (rare) the block's codes for that candidate come from exact fp64
-// comparisons.  The error terms are computed in fp64 exactly as specified.
+// are zero, x and the exact quotient round alike and the fast code stands;
+// an element that is that near takes its code from exact fp64 comparisons
+// (rare for fp32 inputs; bf16 inputs hit it more often).  The error terms are
+// computed in fp64 exactly as specified.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -61,6 +62,63 @@ __device__ __forceinline__ void load16(const void* __restrict__ x, int64_t b, fl
       for (int j = 0; j < 4; ++j) w[4 * i + j] = __uint_as_float(v[j]);
     }
   }
+}
+
+// Squared error of a block (magnitudes aw, aw64 = (double)aw, zero offsets
+// zoff) quantized with block scale code k under tensor scale sg:
+// d_e = |W_e| - c s_g |q_e| rounded once, E = ((d_0^2 + d_1^2) + ...) + d_15^2
+// in fp64.  Codes: hardware E2M1 conversion of the fp32 quotient; an element
+// whose quotient lies near a rounding point is re-decided exactly.
+__device__ __forceinline__ double block_error_for_code(const float aw[16], const double aw64[16],
+                                                       const uint32_t zoff[16], int k, double sg64, float inv_sg) {
+  double err = 0.0;
+  if (k == 0) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) err = err + aw64[e] * aw64[e];
+    return err;
+  }
+  const float c = e4m3_to_f32((uint32_t)k);
+  const double cs = (double)c * sg64;  // exact
+  const float inv = __builtin_amdgcn_rcpf(c) * inv_sg;
+  float q[16];
+  uint32_t tmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float xs[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      xs[e] = aw[8 * h + e] * inv;
+      tmin = min(tmin, (__float_as_uint(xs[e]) << 11) + zoff[8 * h + e]);
+    }
+    uint32_t word = 0;
+    word = NVFP4_CVT_PK_FP4(word, xs[0], xs[1], 0);
+    word = NVFP4_CVT_PK_FP4(word, xs[2], xs[3], 1);
+    word = NVFP4_CVT_PK_FP4(word, xs[4], xs[5], 2);
+    word = NVFP4_CVT_PK_FP4(word, xs[6], xs[7], 3);
+    fp4x8_to_f32(word, q + 8 * h);
+  }
+  const bool fast = inv < 0x1p100f && inv > 0x1p-100f;
+  if (!fast || tmin < kNearLim) {
+    // Only the elements near a rounding point (or all, off the fast range)
+    // are re-decided: bf16 inputs, whose quotients by one scale share a short
+    // denominator, reach this branch in most waves.
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      if (!fast || (__float_as_uint(aw[e] * inv) << 11) + zoff[e] < kNearLim) {
+        const f32x2 ex = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(e2m1_code_exact(aw[e], cs), 1.0f, 0);
+        q[e] = ex.x;
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    // |W| - c s_g |q|: c s_g q is exact, so the fused form rounds once, like
+    // the separate subtraction of the exact product.
+    const double d = __builtin_fma(-cs, (double)q[e], aw64[e]);
+    const double sq = d * d;
+    err = err + sq;
+  }
+  return err;
 }
 
 // kFourOverSix: the candidates are only the scales that map the block
@@ -117,48 +175,7 @@ __global__ __launch_bounds__(256) void quantize_mse_kernel(const void* __restric
     for (int i = 0; i < ncand; ++i) {
       const int k = kFourOverSix ? (i == 0 ? kabs : k4) : kfirst + i;
       if (!kFourOverSix && (k < klo || k > khi) && k != kabs) continue;
-      double err = 0.0;
-      if (k == 0) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) err = err + aw64[e] * aw64[e];
-      } else {
-        const float c = e4m3_to_f32((uint32_t)k);
-        const double cs = (double)c * sg64;  // exact
-        const float inv = __builtin_amdgcn_rcpf(c) * inv_sg;
-        float q[16];
-        uint32_t tmin = 0xFFFFFFFFu;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          float xs[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            xs[e] = aw[8 * h + e] * inv;
-            tmin = min(tmin, (__float_as_uint(xs[e]) << 11) + zoff[8 * h + e]);
-          }
-          uint32_t word = 0;
-          word = NVFP4_CVT_PK_FP4(word, xs[0], xs[1], 0);
-          word = NVFP4_CVT_PK_FP4(word, xs[2], xs[3], 1);
-          word = NVFP4_CVT_PK_FP4(word, xs[4], xs[5], 2);
-          word = NVFP4_CVT_PK_FP4(word, xs[6], xs[7], 3);
-          fp4x8_to_f32(word, q + 8 * h);
-        }
-        const bool fast = inv < 0x1p100f && inv > 0x1p-100f;
-        if (!fast || tmin < kNearLim) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const f32x2 ex = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(e2m1_code_exact(aw[e], cs), 1.0f, 0);
-            q[e] = ex.x;
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          // |W| - c s_g |q|: c s_g q is exact, so the fused form rounds once,
-          // like the separate subtraction of the exact product.
-          const double d = __builtin_fma(-cs, (double)q[e], aw64[e]);
-          const double sq = d * d;
-          err = err + sq;
-        }
-      }
+      const double err = block_error_for_code(aw, aw64, zoff, k, sg64, inv_sg);
       if (best < 0 || err < best_err) {
         best = k;
         best_err = err;
@@ -190,6 +207,135 @@ hipError_t launch_quantize_search(const void* x, bool bf16, bool four_over_six, 
     else NVFP4_QSEARCH(false, false);
   }
 #undef NVFP4_QSEARCH
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- activation scale sweep
+
+// FP8 candidate sweep for a static activation tensor scale ("Tu pipeline
+// NVFP4 ...", section 1, question 3: activation scales are calibrated on
+// recorded activation ranges; section 2, project box: the MSE calibration
+// also sweeps candidate activation scales in FP8).  Candidate c = 0..16 maps
+// the calibration amax's block scale onto E4M3(126 - c) = 448 .. 112:
+// s_c = fp32(amax / (6 E4M3(126 - c))), 1 when amax == 0.  Workgroup
+// (x, y) takes candidates c = y, y + 4, ... (4 or 5 of them, so a small batch
+// still fills the chip and each lane's chain is short); each lane owns one
+// 16-element bf16 block per grid-stride step and accumulates, per candidate,
+// the block's squared error after absmax quantization under s_c (the same
+// arithmetic as the scale searches) in fp64; the workgroup's 4 waves are
+// added in wave order into one fp64 partial per candidate.
+constexpr int kSweepGroups = 4;
+constexpr int kSweepPerGroup = (kSweepCandidates + kSweepGroups - 1) / kSweepGroups;
+
+__device__ __forceinline__ float sweep_candidate(float amax, int c) {
+  if (amax == 0.0f) return 1.0f;
+  return (float)((double)amax / (6.0 * (double)e4m3_to_f32((uint32_t)(kE4M3MaxCode - c))));
+}
+
+__global__ __launch_bounds__(256) void act_sweep_kernel(const u32x4* __restrict__ x, int64_t nblocks,
+                                                        const float* __restrict__ amax_ptr,
+                                                        double* __restrict__ partials) {
+  const float amax = *amax_ptr;
+  const int y = blockIdx.y;
+  float sgs[kSweepPerGroup], inv_sgs[kSweepPerGroup];
+  double acc[kSweepPerGroup];
+#pragma unroll
+  for (int i = 0; i < kSweepPerGroup; ++i) {
+    const int c = y + kSweepGroups * i;
+    sgs[i] = sweep_candidate(amax, c < kSweepCandidates ? c : 0);
+    inv_sgs[i] = 1.0f / sgs[i];
+    acc[i] = 0.0;
+  }
+  const int tid = threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + tid; b < nblocks; b += stride) {
+    float aw[16];
+    float mf = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const u32x4 v = __builtin_nontemporal_load(x + 2 * b + i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        aw[8 * i + 2 * j] = fabsf(bf16_bits_to_f32(v[j] & 0xFFFFu));
+        aw[8 * i + 2 * j + 1] = fabsf(bf16_bits_to_f32(v[j] >> 16));
+      }
+    }
+    double aw64[16];
+    uint32_t zoff[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      mf = fmaxf(mf, aw[e]);
+      aw64[e] = (double)aw[e];
+      zoff[e] = aw[e] == 0.0f ? kZeroOff : kNearOff;
+    }
+    const double m = (double)mf;
+#pragma unroll
+    for (int i = 0; i < kSweepPerGroup; ++i) {
+      if (y + kSweepGroups * i >= kSweepCandidates) continue;  // uniform
+      const double sg64 = (double)sgs[i];
+      const int k = (int)e4m3_code_rne(m / (6.0 * sg64));
+      acc[i] = acc[i] + block_error_for_code(aw, aw64, zoff, k, sg64, inv_sgs[i]);
+    }
+  }
+  __shared__ double red[4][kSweepPerGroup];
+  const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int i = 0; i < kSweepPerGroup; ++i) {
+    double v = acc[i];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    if (lane == 0) red[wave][i] = v;
+  }
+  __syncthreads();
+  if (tid < kSweepPerGroup && y + kSweepGroups * tid < kSweepCandidates) {
+    const int i = tid;
+    partials[(int64_t)blockIdx.x * kSweepCandidates + y + kSweepGroups * i] =
+        ((red[0][i] + red[1][i]) + red[2][i]) + red[3][i];
+  }
+}
+
+// errors[c] += the sum of the np workgroup partials of candidate c (wave
+// c % 4 takes candidate c; lane l adds partials l, l + 64, ... in order,
+// then a fixed butterfly adds the 64 lanes); then the smallest error (ties:
+// lower c) picks the scale.
+__global__ __launch_bounds__(256) void act_sweep_finalize_kernel(const double* __restrict__ partials, int np,
+                                                                 const float* __restrict__ amax_ptr,
+                                                                 double* __restrict__ errors,
+                                                                 float* __restrict__ scale) {
+  __shared__ double tot[kSweepCandidates];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int c = wave; c < kSweepCandidates; c += 4) {
+    double s = 0.0;
+#pragma unroll 4
+    for (int i = lane; i < np; i += 64) s = s + partials[(int64_t)i * kSweepCandidates + c];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    if (lane == 0) {
+      tot[c] = errors[c] + s;
+      errors[c] = tot[c];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int best = 0;
+    for (int c = 1; c < kSweepCandidates; ++c)
+      if (tot[c] < tot[best]) best = c;
+    *scale = sweep_candidate(*amax_ptr, best);
+  }
+}
+
+int act_sweep_partial_count(int64_t n_elems) {
+  int64_t wg = (n_elems / 16 + 255) / 256;
+  if (wg < 1) wg = 1;
+  return wg > 1024 ? 1024 : (int)wg;
+}
+
+hipError_t launch_act_scale_sweep(const uint16_t* x, int64_t n_elems, const float* amax, double* partials,
+                                  double* errors, float* scale, hipStream_t stream) {
+  const int np = act_sweep_partial_count(n_elems);
+  hipLaunchKernelGGL(act_sweep_kernel, dim3((unsigned)np, kSweepGroups), dim3(256), 0, stream,
+                     reinterpret_cast<const u32x4*>(x), n_elems / 16, amax, partials);
+  hipLaunchKernelGGL(act_sweep_finalize_kernel, dim3(1), dim3(256), 0, stream, partials, np, amax, errors, scale);
   return hipGetLastError();
 }
 

@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_LAUNCH, ERR_FLAGS = range(9)
 F32, BF16 = 0, 1
 GLOBAL_COMPUTE, GLOBAL_GIVEN = 0, 1
-OP_QUANTIZE, OP_GEMM_W4A4, OP_GEMV_W4A16, OP_GEMM_W4A4_LORA = 0, 1, 2, 3
+OP_QUANTIZE, OP_GEMM_W4A4, OP_GEMV_W4A16, OP_GEMM_W4A4_LORA, OP_ACT_CALIBRATE = 0, 1, 2, 3, 4
+SWEEP_CANDIDATES = 17
 GEMM_QUANTIZE_ACT, GEMM_REUSE_ACT = 0, 1
 
 # name -> (restype, argtypes); mirrors include/nvfp4.h
@@ -29,6 +30,8 @@ SIGNATURES = {
     "nvfp4_gemv_w4a16": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _SZ, _P]),
     "nvfp4_gemm_w4a4": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _I, _P, _SZ, _P]),
     "nvfp4_gemm_w4a4_lora": (_I, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I, _I, _P, _SZ, _P]),
+    "nvfp4_act_amax": (_I, [_P, _I, _I64, _I64, _P, _P, _SZ, _P]),
+    "nvfp4_act_scale_sweep": (_I, [_P, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
     "nvfp4_workspace_bytes": (_SZ, [_I, _I64, _I64]),
     "nvfp4_status_string": (ctypes.c_char_p, [_I]),
     "nvfp4_version": (_I, []),
@@ -238,3 +241,47 @@ def gemm_workspace_layout(M, K):
 def gemm_lora_l_offset(M, K):
     """Byte offset of the bf16 low-rank activation L [M, r] in the workspace of the fused LoRA product."""
     return 256 + (2 * M * K + 255) // 256 * 256
+
+
+def act_amax(x, amax, workspace=None):
+    """amax = max(amax, max |x|) on the device (x bf16 or fp32 [rows, cols])."""
+    _need_cuda(x, amax)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    rows, cols = x.shape
+    ws = workspace if workspace is not None else _alloc_ws(workspace_bytes(OP_ACT_CALIBRATE, rows, cols), x.device)
+    st = lib().nvfp4_act_amax(_ptr(x), _dtype_code(x.dtype), rows, cols, _ptr(amax), _ptr(ws), ws.numel(), _stream())
+    _check("nvfp4_act_amax", st)
+
+
+def act_scale_sweep(x, amax, errors, scale, workspace=None):
+    """Add one bf16 calibration batch's errors for the 17 candidate static
+    activation scales to `errors` (fp64 [17]) and write the current best scale."""
+    _need_cuda(x, amax, errors, scale)
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("x must be a 2-D bfloat16 tensor")
+    if errors.dtype != torch.float64 or errors.numel() != SWEEP_CANDIDATES:
+        raise ValueError("errors must be a float64 tensor of SWEEP_CANDIDATES elements")
+    rows, cols = x.shape
+    ws = workspace if workspace is not None else _alloc_ws(workspace_bytes(OP_ACT_CALIBRATE, rows, cols), x.device)
+    st = lib().nvfp4_act_scale_sweep(_ptr(x), rows, cols, _ptr(amax), _ptr(errors), _ptr(scale), _ptr(ws),
+                                     ws.numel(), _stream())
+    _check("nvfp4_act_scale_sweep", st)
+
+
+def calibrate_act_scale(batches):
+    """Static activation tensor scale from bf16 calibration batches (all on the
+    GPU): the running amax over every batch, then the FP8 candidate sweep.
+    Returns (scale fp32 [1], errors fp64 [17], amax fp32 [1]) device tensors;
+    pass `scale` as a_global to gemm_w4a4."""
+    if not batches:
+        raise ValueError("no calibration batches")
+    dev = batches[0].device
+    amax = torch.zeros(1, dtype=torch.float32, device=dev)
+    errors = torch.zeros(SWEEP_CANDIDATES, dtype=torch.float64, device=dev)
+    scale = torch.empty(1, dtype=torch.float32, device=dev)
+    for b in batches:
+        act_amax(b, amax)
+    for b in batches:
+        act_scale_sweep(b, amax, errors, scale)
+    return scale, errors, amax

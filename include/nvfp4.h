@@ -78,8 +78,12 @@ enum {
   NVFP4_OP_QUANTIZE = 0,
   NVFP4_OP_GEMM_W4A4 = 1,
   NVFP4_OP_GEMV_W4A16 = 2,
-  NVFP4_OP_GEMM_W4A4_LORA = 3
+  NVFP4_OP_GEMM_W4A4_LORA = 3,
+  NVFP4_OP_ACT_CALIBRATE = 4
 };
+
+/* number of candidate scales of nvfp4_act_scale_sweep */
+enum { NVFP4_SWEEP_CANDIDATES = 17 };
 
 /*
  * nvfp4_quantize_absmax -- NVFP4 encoding with absmax block scales.
@@ -229,9 +233,54 @@ int nvfp4_gemm_w4a4_lora(const void* a, const float* a_global, const uint8_t* w_
                          int64_t M, int64_t N, int64_t K, void* y, int y_dtype, int flags,
                          void* workspace, size_t ws_bytes, void* stream);
 
-/* Workspace size in bytes for an operation: NVFP4_OP_QUANTIZE with
- * (rows, cols), NVFP4_OP_GEMM_W4A4 and NVFP4_OP_GEMM_W4A4_LORA with (M, K),
- * NVFP4_OP_GEMV_W4A16 with (M, N); 0 for an unknown op or negative sizes. */
+/*
+ * nvfp4_act_amax -- running range of calibration activations:
+ * *amax = max(*amax, max |x|).  ("Tu pipeline NVFP4 ...", section 1,
+ * question 3: activation scales come from calibration, which records the
+ * ranges of real activations.)
+ *   x       [rows, cols] of x_dtype (NVFP4_BF16 or NVFP4_F32), 16-byte aligned
+ *   amax    one device fp32, read and written; set it to 0 before the first
+ *           batch
+ *   workspace >= nvfp4_workspace_bytes(NVFP4_OP_ACT_CALIBRATE, rows, cols)
+ *   cols % 16 == 0 (NVFP4_ERR_SHAPE otherwise); rows == 0 is a no-op.
+ */
+int nvfp4_act_amax(const void* x, int x_dtype, int64_t rows, int64_t cols, float* amax,
+                   void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * nvfp4_act_scale_sweep -- FP8 candidate sweep for a static activation
+ * tensor scale s_gA ("Tu pipeline NVFP4 ...", section 2, project box: the MSE
+ * calibration also sweeps candidate activation scales in FP8).  Candidate
+ * c = 0 .. NVFP4_SWEEP_CANDIDATES-1 puts the block scale of the calibration
+ * set's largest block on the E4M3 value v_c = 448, 416, ..., 120, 112 (E4M3
+ * byte 0x7E - c): s_c = fp32(amax / (6 v_c)), and s_c = 1 when amax == 0;
+ * c = 0 is the dynamic rule's s_gA.  For one batch of calibration
+ * activations:
+ *   errors[c] += sum over the batch's 16-element blocks of the squared error
+ *                of the block after the W4A4 activation quantization (absmax
+ *                block scales) with s_gA = s_c, d = |x| - s_b s_c |q| rounded
+ *                once and squared in fp64;
+ *   *scale     = s_c of the smallest errors[c] so far (ties: lower c).
+ *   x       [rows, cols] bf16, 16-byte aligned; cols % 16 == 0
+ *   amax    one device fp32: the running range over ALL calibration batches
+ *           (nvfp4_act_amax over every batch first)
+ *   errors  NVFP4_SWEEP_CANDIDATES device doubles, 8-byte aligned; set them
+ *           to 0 before the first batch; batches accumulate in call order
+ *           (the sums inside one call are in a fixed order, so results are
+ *           reproducible)
+ *   scale   one device fp32, written: pass it as a_global to the W4A4
+ *           products, which then quantize activations in one pass
+ *   workspace >= nvfp4_workspace_bytes(NVFP4_OP_ACT_CALIBRATE, rows, cols)
+ * rows == 0 adds nothing but still writes *scale.
+ */
+int nvfp4_act_scale_sweep(const void* x, int64_t rows, int64_t cols, const float* amax,
+                          double* errors, float* scale, void* workspace, size_t ws_bytes,
+                          void* stream);
+
+/* Workspace size in bytes for an operation: NVFP4_OP_QUANTIZE and
+ * NVFP4_OP_ACT_CALIBRATE with (rows, cols), NVFP4_OP_GEMM_W4A4 and
+ * NVFP4_OP_GEMM_W4A4_LORA with (M, K), NVFP4_OP_GEMV_W4A16 with (M, N); 0 for
+ * an unknown op or negative sizes. */
 size_t nvfp4_workspace_bytes(int op, int64_t rows_or_m, int64_t cols_or_k);
 
 /* Static, NUL-terminated description of a status code. */

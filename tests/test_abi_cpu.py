@@ -25,14 +25,14 @@ def header_functions():
 def test_library_exports_every_declared_symbol():
     L = nv.lib()
     names = header_functions()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(L, n), n
         assert n in nv.SIGNATURES, n
 
 
 def test_status_strings_and_version():
-    assert nv.lib().nvfp4_version() == 10200
+    assert nv.lib().nvfp4_version() == 10300
     for s in range(9):
         assert nv.status_string(s) and nv.status_string(s) != "unknown status"
     assert nv.status_string(99) == "unknown status"
@@ -137,6 +137,29 @@ def test_gemm_lora_validation():
     # the plain product's workspace is too small once L is added
     assert call(wsb=nv.workspace_bytes(nv.OP_GEMM_W4A4, 64, 64)) == nv.ERR_WORKSPACE
     assert call(M=0) == nv.OK
+
+
+def test_calibration_validation():
+    L = nv.lib()
+    W = nv.workspace_bytes(nv.OP_ACT_CALIBRATE, 64, 64)
+    assert W > 0 and W % 256 == 0
+    am = L.nvfp4_act_amax
+    assert am(None, nv.BF16, 4, 64, A4, A16, W, None) == nv.ERR_NULL
+    assert am(A16, nv.BF16, 4, 64, None, A16, W, None) == nv.ERR_NULL
+    assert am(A16, 7, 4, 64, A4, A16, W, None) == nv.ERR_DTYPE
+    assert am(A16, nv.BF16, 4, 40, A4, A16, W, None) == nv.ERR_SHAPE
+    assert am(A16, nv.BF16, -1, 64, A4, A16, W, None) == nv.ERR_SHAPE
+    assert am(A16 + 8, nv.BF16, 4, 64, A4, A16, W, None) == nv.ERR_ALIGN
+    assert am(A16, nv.BF16, 4, 64, A4, A16, 0, None) == nv.ERR_WORKSPACE
+    assert am(A16, nv.BF16, 0, 64, A4, A16, W, None) == nv.OK           # empty: no launch
+    sw = L.nvfp4_act_scale_sweep
+    assert sw(None, 4, 64, A4, A16, A4, A16, W, None) == nv.ERR_NULL
+    assert sw(A16, 4, 64, A4, None, A4, A16, W, None) == nv.ERR_NULL
+    assert sw(A16, 4, 64, A4, A16, None, A16, W, None) == nv.ERR_NULL
+    assert sw(A16, 4, 24, A4, A16, A4, A16, W, None) == nv.ERR_SHAPE
+    assert sw(A16, 4, 64, A4, A4, A4, A16, W, None) == nv.ERR_ALIGN     # errors must be 8-byte aligned
+    assert sw(A16, 4, 64, A4, A16, A4, A16 + 16, W, None) == nv.ERR_ALIGN
+    assert sw(A16, 4, 64, A4, A16, A4, A16, 8, None) == nv.ERR_WORKSPACE
 
 
 def test_python_layer_rejects_mismatched_packed_shapes():
