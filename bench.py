@@ -15,8 +15,9 @@ HBM:
             M = 512 tokens, to_q/k/v 3072x3072 (k, v reuse q's activation),
             MLP up 12288x3072 and down 3072x12288;
   lora      the same block with a fused rank-32 low-rank branch on q/k/v
-            (one 9216x3072 layer), MLP up and MLP down (reported per stage,
-            outside value);
+            (one 9216x3072 layer), MLP up and MLP down, and again as
+            SVDQuant layers (per-channel smoothing folded into the same pass)
+            (reported per stage, outside value);
   calibrate the static activation scale: running amax and the FP8
             candidate sweep over four 512x3072 batches and the 4096x3072
             image-stream input, and the prefill gate product with a
@@ -121,6 +122,7 @@ def main():
     import torch
     from dit_quantization_amd import inputs
     from dit_quantization_amd import nvfp4 as nv
+    from dit_quantization_amd import svdquant
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -343,15 +345,24 @@ def main():
                 down, up = (bf16(t) for t in inputs.lora_factors(32, K, N, 300 + 10 * stream_id + li))
                 wsl = torch.empty(nv.workspace_bytes(nv.OP_GEMM_W4A4_LORA, Ms, K), dtype=torch.uint8, device=dev)
                 out = torch.empty((Ms, N), dtype=torch.bfloat16, device=dev)
-                lora_calls.append((act, wq, down, up, wsl, out))
+                # SVDQuant smoothing multipliers from this layer's channel ranges
+                a_k = torch.zeros(K, dtype=torch.float32, device=dev)
+                nv.channel_amax(act, a_k)
+                _, smooth = svdquant.smoothing(a_k.cpu().numpy(), np.abs(wf).max(axis=0))
+                lora_calls.append((act, wq, down, up, wsl, out, torch.from_numpy(smooth).to(dev)))
                 lora_flops += 2.0 * Ms * N * K + 2.0 * Ms * 32 * (K + N)
             del layers
 
         def dit_block_lora():
-            for act, wq, down, up, wsl, out in lora_calls:
+            for act, wq, down, up, wsl, out, _ in lora_calls:
                 nv.gemm_w4a4(act, *wq, workspace=wsl, out=out, lora=(down, up))
 
+        def dit_block_svdq():
+            for act, wq, down, up, wsl, out, smooth in lora_calls:
+                nv.gemm_w4a4(act, *wq, workspace=wsl, out=out, lora=(down, up), smooth=smooth)
+
         capture("lora_dit_block", dit_block_lora, flops=lora_flops)
+        capture("svdq_dit_block", dit_block_svdq, flops=lora_flops)
 
     torch.cuda.synchronize()
     log(f"[setup] done in {time.time() - t0:.1f}s; stages: {list(stages)}")

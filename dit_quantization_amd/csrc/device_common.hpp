@@ -156,6 +156,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_buf(const void* base, uin
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// SVDQuant smoothing of 8 bf16 values (packed in v) by the per-channel fp32
+// multipliers m[0..7]: bf16(fp32(x * m)), both roundings to nearest even
+// (the fp32 product of a bf16 and an fp32 is correctly rounded).
+__device__ __forceinline__ u32x4 smooth8(u32x4 v, f32x4 m0, f32x4 m1) {
+  u32x4 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float a = bf16_bits_to_f32(v[j] & 0xFFFFu) * (j < 2 ? m0[2 * j] : m1[2 * j - 4]);
+    const float b = bf16_bits_to_f32(v[j] >> 16) * (j < 2 ? m0[2 * j + 1] : m1[2 * j - 3]);
+    o[j] = f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+  }
+  return o;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

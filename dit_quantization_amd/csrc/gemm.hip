@@ -94,11 +94,17 @@ hipError_t launch_act_quant_f16(const uint16_t* a, int64_t n_elems, const float*
 // split the result is stored as bf16 (RNE) L [M, 16 RT], otherwise as fp32
 // partial sums [splits, M, 16 RT] that lora_reduce_kernel adds in split
 // order.
-template <int RT>
+//
+// SMOOTH (SVDQuant, same section: outliers moved from the activation into
+// the weights channel by channel): every loaded x chunk is first replaced by
+// bf16(x_k mult_k) with the per-channel fp32 multipliers, and both the
+// quantizer and the down projection see that smoothed activation.
+template <int RT, bool SMOOTH>
 __global__ __launch_bounds__(256) void act_quant_lora_kernel(const uint16_t* __restrict__ a,
                                                              const float* __restrict__ sg_ptr,
                                                              const uint16_t* __restrict__ down, int M, int K,
-                                                             int splits, int cps, uint16_t* __restrict__ a_hat,
+                                                             int splits, int cps, const float* __restrict__ mult,
+                                                             uint16_t* __restrict__ a_hat,
                                                              uint16_t* __restrict__ lora_l,
                                                              float* __restrict__ partial) {
   constexpr int R = 16 * RT;
@@ -114,18 +120,23 @@ __global__ __launch_bounds__(256) void act_quant_lora_kernel(const uint16_t* __r
   const double six_sg = 6.0 * (double)sg;
   const __amdgpu_buffer_rsrc_t abuf = make_buf(a + (int64_t)m0 * K, (uint32_t)(rows * K * 2));
   const __amdgpu_buffer_rsrc_t dbuf = make_buf(down, (uint32_t)(R * K * 2));
+  const __amdgpu_buffer_rsrc_t mbuf = make_buf(mult, SMOOTH ? (uint32_t)(K * 4) : 0u);
   const int nch = K / 32;
   const int cbeg = split * cps, cend = min(cbeg + cps, nch);
   f32x4 acc[RT];
 #pragma unroll
   for (int jt = 0; jt < RT; ++jt) acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int c0 = cbeg + wave; c0 < cend; c0 += 4 * U) {  // wave-uniform
-    u32x4 v[U], d[U][RT];
+    u32x4 v[U], d[U][RT], sm[U][2];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = c0 + 4 * u;
       const int k = 32 * c + 8 * g;
       v[u] = __builtin_amdgcn_raw_buffer_load_b128(abuf, c < cend ? (row * K + k) * 2 : kBufOOB, 0, kBufNT);
+      if constexpr (SMOOTH) {
+        sm[u][0] = __builtin_amdgcn_raw_buffer_load_b128(mbuf, c < cend ? k * 4 : kBufOOB, 0, 0);
+        sm[u][1] = __builtin_amdgcn_raw_buffer_load_b128(mbuf, c < cend ? k * 4 + 16 : kBufOOB, 0, 0);
+      }
 #pragma unroll
       for (int jt = 0; jt < RT; ++jt)
         d[u][jt] = __builtin_amdgcn_raw_buffer_load_b128(dbuf, c < cend ? ((16 * jt + row) * K + k) * 2 : kBufOOB,
@@ -135,6 +146,8 @@ __global__ __launch_bounds__(256) void act_quant_lora_kernel(const uint16_t* __r
     for (int u = 0; u < U; ++u) {
       const int c = c0 + 4 * u;
       const int k = 32 * c + 8 * g;
+      if constexpr (SMOOTH)
+        v[u] = smooth8(v[u], __builtin_bit_cast(f32x4, sm[u][0]), __builtin_bit_cast(f32x4, sm[u][1]));
       float w[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -206,15 +219,20 @@ int lora_splits(int64_t M, int64_t K) {
 }
 
 hipError_t launch_act_quant_lora(const uint16_t* a, const float* sg, const uint16_t* down, int rank, int64_t M,
-                                 int64_t K, uint16_t* a_hat, uint16_t* lora_l, float* partial, hipStream_t stream) {
+                                 int64_t K, const float* mult, uint16_t* a_hat, uint16_t* lora_l, float* partial,
+                                 hipStream_t stream) {
   if (M == 0) return hipSuccess;
   const int splits = lora_splits(M, K);
   const int nch = (int)(K / 32);
   const int cps = (nch + splits - 1) / splits;
   const dim3 grid((unsigned)(((M + 15) / 16) * splits));
-#define NVFP4_AQL(RT)                                                                                             \
-  hipLaunchKernelGGL((act_quant_lora_kernel<RT>), grid, dim3(256), 0, stream, a, sg, down, (int)M, (int)K, splits, \
-                     cps, a_hat, lora_l, partial)
+#define NVFP4_AQL(RT)                                                                                         \
+  if (mult)                                                                                                   \
+    hipLaunchKernelGGL((act_quant_lora_kernel<RT, true>), grid, dim3(256), 0, stream, a, sg, down, (int)M,    \
+                       (int)K, splits, cps, mult, a_hat, lora_l, partial);                                    \
+  else                                                                                                        \
+    hipLaunchKernelGGL((act_quant_lora_kernel<RT, false>), grid, dim3(256), 0, stream, a, sg, down, (int)M,   \
+                       (int)K, splits, cps, mult, a_hat, lora_l, partial)
   switch (rank / 16) {
     case 1: NVFP4_AQL(1); break;
     case 2: NVFP4_AQL(2); break;

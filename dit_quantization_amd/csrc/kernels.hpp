@@ -13,6 +13,10 @@ constexpr int kSweepCandidates = 17;  // static activation scale candidates, E4M
 int amax_partial_count(int64_t n_elems, bool bf16);
 hipError_t launch_global_scale(const void* x, bool bf16, int64_t n_elems, float* partials, float* sg_out,
                                hipStream_t stream);
+hipError_t launch_global_scale_smooth(const uint16_t* x, int64_t rows, int64_t K, const float* mult,
+                                      float* partials, float* sg_out, hipStream_t stream);
+hipError_t launch_channel_amax(const void* x, bool bf16, int64_t rows, int64_t cols, float* amax,
+                               hipStream_t stream);
 hipError_t launch_running_amax(const void* x, bool bf16, int64_t n_elems, float* partials, float* amax,
                                hipStream_t stream);
 int act_sweep_partial_count(int64_t n_elems);
@@ -31,8 +35,10 @@ hipError_t launch_act_quant_f16(const uint16_t* a, int64_t n_elems, const float*
 // K ranges the fused activation-quantization + LoRA-down pass splits each
 // 16-row tile into; splits > 1 needs fp32 partials of splits * M * rank.
 int lora_splits(int64_t M, int64_t K);
+// mult != nullptr: SVDQuant smoothing, the pass works on bf16(x_k mult_k).
 hipError_t launch_act_quant_lora(const uint16_t* a, const float* sg, const uint16_t* down, int rank, int64_t M,
-                                 int64_t K, uint16_t* a_hat, uint16_t* lora_l, float* partial, hipStream_t stream);
+                                 int64_t K, const float* mult, uint16_t* a_hat, uint16_t* lora_l, float* partial,
+                                 hipStream_t stream);
 hipError_t launch_gemm_w4a4(const uint16_t* a_hat, const float* sga, const uint8_t* codes, const uint8_t* scales,
                             const float* sgw, int64_t M, int64_t N, int64_t K, void* y, bool bf16_out,
                             const uint16_t* lora_l, const uint16_t* lora_up, int rank, hipStream_t stream);

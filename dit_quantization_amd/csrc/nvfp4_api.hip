@@ -11,7 +11,7 @@ namespace {
 
 using namespace nvfp4;
 
-constexpr int kVersion = 1 * 10000 + 3 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 4 * 100 + 0;
 static_assert(kSweepCandidates == NVFP4_SWEEP_CANDIDATES, "candidate count of the activation scale sweep");
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -92,8 +92,9 @@ size_t calibrate_ws_bytes(int64_t n) {
 }
 
 int gemm_common(const void* a, const float* a_global, const uint8_t* w_codes, const uint8_t* w_scales,
-                const float* w_global, const void* lora_down, const void* lora_up, int rank, int64_t M, int64_t N,
-                int64_t K, void* y, int y_dtype, int flags, void* workspace, size_t ws_bytes, void* stream) {
+                const float* w_global, const float* smooth, const void* lora_down, const void* lora_up, int rank,
+                int64_t M, int64_t N, int64_t K, void* y, int y_dtype, int flags, void* workspace, size_t ws_bytes,
+                void* stream) {
   const bool reuse = (flags & NVFP4_GEMM_REUSE_ACT) != 0;
   const bool lora = rank != 0;
   if ((!a && !reuse) || !w_codes || !w_scales || !w_global || !y || !workspace) return NVFP4_ERR_NULL;
@@ -109,6 +110,7 @@ int gemm_common(const void* a, const float* a_global, const uint8_t* w_codes, co
       (a_global && !aligned(a_global, 4)) || !aligned(y, 16) || !aligned(workspace, 256))
     return NVFP4_ERR_ALIGN;
   if (lora && ((!reuse && !aligned(lora_down, 16)) || !aligned(lora_up, 16))) return NVFP4_ERR_ALIGN;
+  if (smooth && !reuse && !aligned(smooth, 16)) return NVFP4_ERR_ALIGN;
   if (ws_bytes < (lora ? gemm_lora_ws_bytes(M, K) : gemm_ws_bytes(M, K))) return NVFP4_ERR_WORKSPACE;
   if (M == 0 || N == 0) return NVFP4_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -125,13 +127,15 @@ int gemm_common(const void* a, const float* a_global, const uint8_t* w_codes, co
     hipError_t e = hipSuccess;
     if (a_global) {
       e = hipMemcpyAsync(sga, a_global, sizeof(float), hipMemcpyDeviceToDevice, s);
+    } else if (smooth) {
+      e = launch_global_scale_smooth(reinterpret_cast<const uint16_t*>(a), M, K, smooth, partials, sga, s);
     } else {
       e = launch_global_scale(a, true, M * K, partials, sga, s);
     }
     if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
     const uint16_t* ab = reinterpret_cast<const uint16_t*>(a);
-    e = lora ? launch_act_quant_lora(ab, sga, reinterpret_cast<const uint16_t*>(lora_down), rank, M, K, a_hat,
-                                     lora_l, lora_partial, s)
+    e = lora ? launch_act_quant_lora(ab, sga, reinterpret_cast<const uint16_t*>(lora_down), rank, M, K, smooth,
+                                     a_hat, lora_l, lora_partial, s)
              : launch_act_quant_f16(ab, M * K, sga, a_hat, s);
     if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
   }
@@ -229,8 +233,8 @@ int nvfp4_gemv_w4a16(const void* x, const uint8_t* w_codes, const uint8_t* w_sca
 int nvfp4_gemm_w4a4(const void* a, const float* a_global, const uint8_t* w_codes, const uint8_t* w_scales,
                     const float* w_global, int64_t M, int64_t N, int64_t K, void* y, int y_dtype, int flags,
                     void* workspace, size_t ws_bytes, void* stream) {
-  return gemm_common(a, a_global, w_codes, w_scales, w_global, nullptr, nullptr, 0, M, N, K, y, y_dtype, flags,
-                     workspace, ws_bytes, stream);
+  return gemm_common(a, a_global, w_codes, w_scales, w_global, nullptr, nullptr, nullptr, 0, M, N, K, y, y_dtype,
+                     flags, workspace, ws_bytes, stream);
 }
 
 int nvfp4_gemm_w4a4_lora(const void* a, const float* a_global, const uint8_t* w_codes, const uint8_t* w_scales,
@@ -239,8 +243,30 @@ int nvfp4_gemm_w4a4_lora(const void* a, const float* a_global, const uint8_t* w_
                          void* stream) {
   if (rank <= 0) return NVFP4_ERR_SHAPE;
   if (rank > kMaxLoraRank) return NVFP4_ERR_UNSUPPORTED;
-  return gemm_common(a, a_global, w_codes, w_scales, w_global, lora_down, lora_up, (int)rank, M, N, K, y, y_dtype,
-                     flags, workspace, ws_bytes, stream);
+  return gemm_common(a, a_global, w_codes, w_scales, w_global, nullptr, lora_down, lora_up, (int)rank, M, N, K, y,
+                     y_dtype, flags, workspace, ws_bytes, stream);
+}
+
+int nvfp4_gemm_w4a4_svdq(const void* a, const float* a_global, const uint8_t* w_codes, const uint8_t* w_scales,
+                         const float* w_global, const float* smooth, const void* lora_down, const void* lora_up,
+                         int64_t rank, int64_t M, int64_t N, int64_t K, void* y, int y_dtype, int flags,
+                         void* workspace, size_t ws_bytes, void* stream) {
+  if (!smooth && !(flags & NVFP4_GEMM_REUSE_ACT)) return NVFP4_ERR_NULL;
+  if (rank <= 0) return NVFP4_ERR_SHAPE;
+  if (rank > kMaxLoraRank) return NVFP4_ERR_UNSUPPORTED;
+  return gemm_common(a, a_global, w_codes, w_scales, w_global, smooth, lora_down, lora_up, (int)rank, M, N, K, y,
+                     y_dtype, flags, workspace, ws_bytes, stream);
+}
+
+int nvfp4_channel_amax(const void* x, int x_dtype, int64_t rows, int64_t cols, float* amax, void* stream) {
+  if (!x || !amax) return NVFP4_ERR_NULL;
+  if (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
+  if (rows < 0 || cols < 0 || !mul_ok(rows, cols) || cols % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (cols > (int64_t)1 << 30) return NVFP4_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(amax, 4)) return NVFP4_ERR_ALIGN;
+  clear_error();
+  return launch_status(launch_channel_amax(x, x_dtype == NVFP4_BF16, rows, cols, amax,
+                                           reinterpret_cast<hipStream_t>(stream)));
 }
 
 int nvfp4_act_amax(const void* x, int x_dtype, int64_t rows, int64_t cols, float* amax, void* workspace,

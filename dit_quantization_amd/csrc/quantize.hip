@@ -41,6 +41,79 @@ __global__ __launch_bounds__(256) void amax_partial_kernel(const void* __restric
   if (threadIdx.x == 0) partials[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
+// The same over the SVDQuant-smoothed bf16 activation bf16(x_k m_k) of a
+// row-major [rows, K] tensor (K % 8 == 0): rounding is monotonic, so the
+// largest smoothed magnitude is the smoothed value of the largest |x m|.
+__global__ __launch_bounds__(256) void amax_smooth_partial_kernel(const u32x4* __restrict__ x, int64_t n_vec,
+                                                                  const f32x4* __restrict__ mult, int kvec,
+                                                                  float* __restrict__ partials) {
+  float m = 0.0f;
+  int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_vec; i += stride) {
+    const u32x4 v = __builtin_nontemporal_load(&x[i]);
+    const int kv = (int)(i % kvec);
+    const u32x4 h = smooth8(v, mult[2 * kv], mult[2 * kv + 1]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      m = fmaxf(m, fabsf(bf16_bits_to_f32(h[j] & 0xFFFFu)));
+      m = fmaxf(m, fabsf(bf16_bits_to_f32(h[j] >> 16)));
+    }
+  }
+  __shared__ float red[4];
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) partials[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// Per-channel running range of a row-major [rows, cols] tensor (cols % 8 ==
+// 0): amax[k] = max(amax[k], max_r |x[r][k]|).  A thread owns 8 consecutive
+// columns of a stripe of rows; the column maxima meet through unsigned
+// atomic max on the float bits (exact and order-free for non-negative
+// floats).
+template <bool kBF16>
+__global__ __launch_bounds__(256) void channel_amax_kernel(const void* __restrict__ x, int64_t rows, int cols,
+                                                           float* __restrict__ amax) {
+  const int c0 = (blockIdx.x * 256 + threadIdx.x) * 8;
+  if (c0 >= cols) return;
+  float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+    if constexpr (kBF16) {
+      const u32x4 v = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(x) + r * cols + c0));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        m[2 * j] = fmaxf(m[2 * j], fabsf(bf16_bits_to_f32(v[j] & 0xFFFFu)));
+        m[2 * j + 1] = fmaxf(m[2 * j + 1], fabsf(bf16_bits_to_f32(v[j] >> 16)));
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32x4 v = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(x) + r * cols + c0) + h);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m[4 * h + j] = fmaxf(m[4 * h + j], fabsf(__uint_as_float(v[j])));
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) atomicMax(reinterpret_cast<unsigned int*>(amax) + c0 + j, __float_as_uint(m[j]));
+}
+
+hipError_t launch_channel_amax(const void* x, bool bf16, int64_t rows, int64_t cols, float* amax,
+                               hipStream_t stream) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  const unsigned gx = (unsigned)((cols / 8 + 255) / 256);
+  int64_t gy = (1024 + gx - 1) / gx;
+  if (gy > rows) gy = rows;
+  const dim3 grid(gx, (unsigned)gy);
+  if (bf16)
+    hipLaunchKernelGGL(channel_amax_kernel<true>, grid, dim3(256), 0, stream, x, rows, (int)cols, amax);
+  else
+    hipLaunchKernelGGL(channel_amax_kernel<false>, grid, dim3(256), 0, stream, x, rows, (int)cols, amax);
+  return hipGetLastError();
+}
+
 // kRunningMax: out = max(out, amax) (a running calibration range) instead of
 // out = s_g(amax).
 template <bool kRunningMax>
@@ -79,6 +152,15 @@ hipError_t launch_global_scale(const void* x, bool bf16, int64_t n_elems, float*
                                hipStream_t stream) {
   int np = amax_partial_count(n_elems, bf16);
   launch_amax_partials(x, bf16, n_elems, partials, np, stream);
+  hipLaunchKernelGGL(amax_finalize_kernel<false>, dim3(1), dim3(256), 0, stream, partials, np, sg_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_global_scale_smooth(const uint16_t* x, int64_t rows, int64_t K, const float* mult,
+                                      float* partials, float* sg_out, hipStream_t stream) {
+  int np = amax_partial_count(rows * K, true);
+  hipLaunchKernelGGL(amax_smooth_partial_kernel, dim3(np), dim3(256), 0, stream, reinterpret_cast<const u32x4*>(x),
+                     rows * K / 8, reinterpret_cast<const f32x4*>(mult), (int)(K / 8), partials);
   hipLaunchKernelGGL(amax_finalize_kernel<false>, dim3(1), dim3(256), 0, stream, partials, np, sg_out);
   return hipGetLastError();
 }

@@ -30,6 +30,9 @@ SIGNATURES = {
     "nvfp4_gemv_w4a16": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _SZ, _P]),
     "nvfp4_gemm_w4a4": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _I, _P, _SZ, _P]),
     "nvfp4_gemm_w4a4_lora": (_I, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I, _I, _P, _SZ, _P]),
+    "nvfp4_gemm_w4a4_svdq": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I, _I, _P, _SZ,
+                                  _P]),
+    "nvfp4_channel_amax": (_I, [_P, _I, _I64, _I64, _P, _P]),
     "nvfp4_act_amax": (_I, [_P, _I, _I64, _I64, _P, _P, _SZ, _P]),
     "nvfp4_act_scale_sweep": (_I, [_P, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
     "nvfp4_workspace_bytes": (_SZ, [_I, _I64, _I64]),
@@ -191,11 +194,13 @@ def gemv_w4a16(x, w_codes, w_scales, w_global, out_dtype=torch.bfloat16, workspa
 
 
 def gemm_w4a4(a, w_codes, w_scales, w_global, a_global=None, out_dtype=torch.bfloat16, workspace=None,
-              out=None, reuse_act=False, lora=None):
+              out=None, reuse_act=False, lora=None, smooth=None):
     """y = quant(a) W^T with per-call NVFP4 quantization of bf16 a [M, K].
 
     lora=(down [r, K], up [N, r]) (bf16) adds the 16-bit low-rank term
     (a down^T) up^T, fused into the same pass (r = 16, 32, ..., 128).
+    smooth=[K] fp32 multipliers (with lora): the SVDQuant layer, whose input
+    is bf16(a * smooth) (see svdquant.prepare).
 
     a_global=None computes the activation's tensor scale on the device.
     The workspace (returned contents documented in include/nvfp4.h) may be
@@ -212,6 +217,8 @@ def gemm_w4a4(a, w_codes, w_scales, w_global, a_global=None, out_dtype=torch.bfl
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a.device)
     flags = GEMM_REUSE_ACT if reuse_act else GEMM_QUANTIZE_ACT
+    if smooth is not None and lora is None:
+        raise ValueError("smooth needs the low-rank factors (lora=)")
     if lora is None:
         ws = workspace if workspace is not None else _alloc_ws(workspace_bytes(OP_GEMM_W4A4, M, K), a.device)
         st = lib().nvfp4_gemm_w4a4(_ptr(a), _ptr(a_global), _ptr(w_codes), _ptr(w_scales), _ptr(w_global), M, N, K,
@@ -226,10 +233,19 @@ def gemm_w4a4(a, w_codes, w_scales, w_global, a_global=None, out_dtype=torch.bfl
     if down.shape != (r, K) or up.shape != (N, r) or not down.is_contiguous() or not up.is_contiguous():
         raise ValueError("lora = (down [r, K], up [N, r]) must be contiguous with matching sizes")
     ws = workspace if workspace is not None else _alloc_ws(workspace_bytes(OP_GEMM_W4A4_LORA, M, K), a.device)
-    st = lib().nvfp4_gemm_w4a4_lora(_ptr(a), _ptr(a_global), _ptr(w_codes), _ptr(w_scales), _ptr(w_global),
-                                    _ptr(down), _ptr(up), r, M, N, K, _ptr(out), _dtype_code(out.dtype), flags,
-                                    _ptr(ws), ws.numel(), _stream())
-    _check("nvfp4_gemm_w4a4_lora", st)
+    if smooth is None:
+        st = lib().nvfp4_gemm_w4a4_lora(_ptr(a), _ptr(a_global), _ptr(w_codes), _ptr(w_scales), _ptr(w_global),
+                                        _ptr(down), _ptr(up), r, M, N, K, _ptr(out), _dtype_code(out.dtype), flags,
+                                        _ptr(ws), ws.numel(), _stream())
+        _check("nvfp4_gemm_w4a4_lora", st)
+        return out
+    _need_cuda(smooth)
+    if smooth.dtype != torch.float32 or smooth.shape != (K,):
+        raise ValueError("smooth must be a float32 [K] tensor")
+    st = lib().nvfp4_gemm_w4a4_svdq(_ptr(a), _ptr(a_global), _ptr(w_codes), _ptr(w_scales), _ptr(w_global),
+                                    _ptr(smooth), _ptr(down), _ptr(up), r, M, N, K, _ptr(out),
+                                    _dtype_code(out.dtype), flags, _ptr(ws), ws.numel(), _stream())
+    _check("nvfp4_gemm_w4a4_svdq", st)
     return out
 
 
@@ -285,3 +301,12 @@ def calibrate_act_scale(batches):
     for b in batches:
         act_scale_sweep(b, amax, errors, scale)
     return scale, errors, amax
+
+
+def channel_amax(x, amax):
+    """amax[k] = max(amax[k], max_r |x[r, k]|) on the device (x bf16 or fp32 [rows, cols], amax fp32 [cols])."""
+    _need_cuda(x, amax)
+    if x.dim() != 2 or amax.dtype != torch.float32 or amax.shape != (x.shape[1],):
+        raise ValueError("x [rows, cols] and amax float32 [cols]")
+    st = lib().nvfp4_channel_amax(_ptr(x), _dtype_code(x.dtype), x.shape[0], x.shape[1], _ptr(amax), _stream())
+    _check("nvfp4_channel_amax", st)

@@ -234,6 +234,45 @@ int nvfp4_gemm_w4a4_lora(const void* a, const float* a_global, const uint8_t* w_
                          void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * nvfp4_gemm_w4a4_svdq -- the low-rank W4A4 product on an SVDQuant-smoothed
+ * activation ("NVFP4 en difusion ...", section 3: SVDQuant moves activation
+ * outliers into the weights by scaling channel by channel, then keeps a
+ * 16-bit low-rank SVD component of the scaled weights beside the 4-bit
+ * residual; that component has a LoRA's shape and runs in the same fused
+ * pass).  The layer's input becomes x^[m,k] = bf16(fp32(a[m,k] * smooth[k]))
+ * (round to nearest even twice), and then
+ *   y = W4A4(x^, R^) + bf16(x^ lora_down^T) lora_up^T
+ * exactly as nvfp4_gemm_w4a4_lora computes it on x^: s_gA is computed from
+ * x^ (or given: a scale calibrated on x^), and the workspace holds the
+ * quantized x^ and L.
+ *   smooth   [K] device fp32 multipliers 1/lambda_k (16-byte aligned); the
+ *            weights were prepared as W' = W diag(lambda), split into the
+ *            rank-r factors (lora_up [N, r] lora_down [r, K], bf16) and the
+ *            residual R = W' - lora_up lora_down, quantized to w_codes,
+ *            w_scales, w_global.  A user LoRA (A, B) can ride along as extra
+ *            rank: down rows A diag(lambda), up columns B.
+ *   everything else as nvfp4_gemm_w4a4_lora; smooth is not read with
+ *   NVFP4_GEMM_REUSE_ACT (the earlier call's x^ is reused).
+ */
+int nvfp4_gemm_w4a4_svdq(const void* a, const float* a_global, const uint8_t* w_codes,
+                         const uint8_t* w_scales, const float* w_global, const float* smooth,
+                         const void* lora_down, const void* lora_up, int64_t rank,
+                         int64_t M, int64_t N, int64_t K, void* y, int y_dtype, int flags,
+                         void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * nvfp4_channel_amax -- per-channel running range of calibration
+ * activations (or of a weight's input columns), the statistic SVDQuant's
+ * smoothing needs: amax[k] = max(amax[k], max_r |x[r, k]|).
+ *   x      [rows, cols] of x_dtype (NVFP4_BF16 or NVFP4_F32), 16-byte aligned
+ *   amax   [cols] device fp32, read and written; zero it before the first
+ *          batch.  The result does not depend on the order of the updates.
+ *   cols % 16 == 0 (NVFP4_ERR_SHAPE otherwise); rows == 0 is a no-op.
+ */
+int nvfp4_channel_amax(const void* x, int x_dtype, int64_t rows, int64_t cols, float* amax,
+                       void* stream);
+
+/*
  * nvfp4_act_amax -- running range of calibration activations:
  * *amax = max(*amax, max |x|).  ("Tu pipeline NVFP4 ...", section 1,
  * question 3: activation scales come from calibration, which records the

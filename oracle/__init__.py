@@ -52,6 +52,10 @@ def _load():
     lib.oracle_lora_term.argtypes = [P, P, P, i64, i64, P, P, i64, P, P, ctypes.c_int]
     lib.oracle_act_scale_errors.restype = ctypes.c_int
     lib.oracle_act_scale_errors.argtypes = [P, i64, ctypes.c_float, P, ctypes.c_int]
+    lib.oracle_smooth_factors.restype = None
+    lib.oracle_smooth_factors.argtypes = [P, P, i64, P, P]
+    lib.oracle_smooth_act.restype = None
+    lib.oracle_smooth_act.argtypes = [P, P, i64, i64, P]
     lib.oracle_4o6_scale_code.restype = ctypes.c_int
     lib.oracle_4o6_scale_code.argtypes = [P, ctypes.c_float]
     lib.oracle_block_error.restype = ctypes.c_double
@@ -259,6 +263,31 @@ def act_scale_sweep(batches, amax=None, threads=None):
         if err[c] < err[best]:
             best = c
     return err, best, act_scale_candidates(amax)[best], amax
+
+
+def smooth_factors(act_amax, w_amax):
+    """SVDQuant per-channel smoothing (reading R14): (lambda, mult) fp32 [K],
+    lambda_k = fp32(sqrt(a_k / w_k)) (1 if either is 0), mult_k = fp32(1 / lambda_k)."""
+    a = np.ascontiguousarray(act_amax, dtype=np.float32)
+    w = np.ascontiguousarray(w_amax, dtype=np.float32)
+    if a.shape != w.shape or a.ndim != 1:
+        raise ValueError("smooth_factors: two [K] vectors")
+    lam = np.empty_like(a)
+    mult = np.empty_like(a)
+    _load().oracle_smooth_factors(_ptr(a), _ptr(w), a.size, _ptr(lam), _ptr(mult))
+    return lam, mult
+
+
+def smooth_act(x, mult):
+    """x^ = bf16(fp32(x * mult)) per input channel, as float32 [M, K]."""
+    x = _as_f32_2d(x)
+    mult = np.ascontiguousarray(mult, dtype=np.float32)
+    M, K = x.shape
+    if mult.shape != (K,):
+        raise ValueError("smooth_act: mult must be [K]")
+    out = np.empty_like(x)
+    _load().oracle_smooth_act(_ptr(x), _ptr(mult), M, K, _ptr(out))
+    return out
 
 
 def bf16_rne_from_f64(v):

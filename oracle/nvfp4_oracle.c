@@ -32,6 +32,7 @@
  *   R11 four-over-six: candidates max/(6 s_g) and max/(4 s_g), each rounded
  *   to E4M3; the R5 error decides, ties keep the smaller scale.
  *   R13 activation scale sweep: see oracle_act_scale_errors.
+ *   R14 SVDQuant smoothing: see oracle_smooth_factors and oracle_smooth_act.
  */
 #include <math.h>
 #include <stdint.h>
@@ -350,4 +351,45 @@ int oracle_act_scale_errors(const float* x, int64_t n, float amax, double* err, 
         err[c] = e;
     }
     return 0;
+}
+
+/* ---- SVDQuant smoothing ------------------------------------------------ */
+
+/* Nearest bf16 value (8 significant bits, fp32's exponent range) to x, ties
+ * to the even significand: x = f 2^e with f in [0.5, 1), so the spacing of
+ * bf16 values around x is 2^(e - 8) (2^-133 below the normal range). */
+static double bf16_nearest(double x) {
+    if (x == 0.0 || !isfinite(x)) return x;
+    int e;
+    (void)frexp(x, &e);
+    int q = (e < -125 ? -125 : e) - 8;
+    return ldexp(nearbyint(ldexp(x, -q)), q);
+}
+
+/* Per-input-channel smoothing factors [P3 sec.3: SVDQuant first moves the
+ * activation outliers into the weights by scaling channel by channel].
+ * Reading R14: lambda_k = sqrt(a_k / w_k) (migration strength 1/2), a_k the
+ * calibration max |x| of channel k, w_k the max |W| of input column k, each
+ * operation in fp64 and the result rounded to fp32; lambda_k = 1 when a_k or
+ * w_k is 0.  mult_k = fp32(1 / lambda_k) is what the activation is
+ * multiplied by. */
+void oracle_smooth_factors(const float* a_amax, const float* w_amax, int64_t K, float* lambda, float* mult) {
+    for (int64_t k = 0; k < K; ++k) {
+        double a = (double)a_amax[k], w = (double)w_amax[k];
+        float l = (a == 0.0 || w == 0.0) ? 1.0f : (float)sqrt(a / w);
+        lambda[k] = l;
+        mult[k] = (float)(1.0 / (double)l);
+    }
+}
+
+/* Smoothed activation x^_{m,k} = bf16(fp32(x_{m,k} mult_k)) (reading R14:
+ * the layer's 16-bit input after the folded per-channel scale; the product
+ * of a bf16 and an fp32 is exact in fp64, so the fp32 rounding is the
+ * correctly rounded product). */
+void oracle_smooth_act(const float* x, const float* mult, int64_t M, int64_t K, float* out) {
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k) {
+            float p = (float)((double)x[m * K + k] * (double)mult[k]);
+            out[m * K + k] = (float)bf16_nearest((double)p);
+        }
 }

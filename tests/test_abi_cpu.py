@@ -25,14 +25,14 @@ def header_functions():
 def test_library_exports_every_declared_symbol():
     L = nv.lib()
     names = header_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(L, n), n
         assert n in nv.SIGNATURES, n
 
 
 def test_status_strings_and_version():
-    assert nv.lib().nvfp4_version() == 10300
+    assert nv.lib().nvfp4_version() == 10400
     for s in range(9):
         assert nv.status_string(s) and nv.status_string(s) != "unknown status"
     assert nv.status_string(99) == "unknown status"
@@ -137,6 +137,30 @@ def test_gemm_lora_validation():
     # the plain product's workspace is too small once L is added
     assert call(wsb=nv.workspace_bytes(nv.OP_GEMM_W4A4, 64, 64)) == nv.ERR_WORKSPACE
     assert call(M=0) == nv.OK
+
+
+def test_svdq_and_channel_amax_validation():
+    L = nv.lib()
+    f = L.nvfp4_gemm_w4a4_svdq
+    W = 1 << 30
+    Q, R = nv.GEMM_QUANTIZE_ACT, nv.GEMM_REUSE_ACT
+
+    def call(smooth=A16, rank=32, flags=Q, M=64, K=64):
+        return f(A16, None, A16, A16, A4, smooth, A16, A16, rank, M, 64, K, A16, nv.BF16, flags, A16, W, None)
+
+    assert call(smooth=None) == nv.ERR_NULL
+    assert call(smooth=None, flags=R, M=0) == nv.OK            # reuse: smooth unused
+    assert call(smooth=A16 + 4) == nv.ERR_ALIGN
+    assert call(rank=0) == nv.ERR_SHAPE
+    assert call(rank=24) == nv.ERR_UNSUPPORTED
+    assert call(K=96) == nv.ERR_UNSUPPORTED
+    assert call(M=0) == nv.OK
+    c = L.nvfp4_channel_amax
+    assert c(None, nv.BF16, 4, 64, A4, None) == nv.ERR_NULL
+    assert c(A16, 3, 4, 64, A4, None) == nv.ERR_DTYPE
+    assert c(A16, nv.BF16, 4, 24, A4, None) == nv.ERR_SHAPE
+    assert c(A16 + 4, nv.BF16, 4, 64, A4, None) == nv.ERR_ALIGN
+    assert c(A16, nv.BF16, 0, 64, A4, None) == nv.OK
 
 
 def test_calibration_validation():

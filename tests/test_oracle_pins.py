@@ -465,3 +465,43 @@ def test_act_scale_sweep_accumulates_batches_in_order():
 def test_act_scale_sweep_zero_input():
     err, best, scale, amax = oracle.act_scale_sweep([np.zeros((4, 32), dtype=np.float32)])
     assert amax == 0.0 and best == 0 and scale == 1.0 and np.all(err == 0)
+
+
+# ---------------------------------------------------------------- SVDQuant smoothing (R14)
+
+def _fp32_neighbours(v):
+    v = np.float32(v)
+    return np.nextafter(v, np.float32(0)), np.nextafter(v, np.float32(np.inf))
+
+
+def test_smooth_factors_are_correctly_rounded_sqrt():
+    g = inputs.rng(51)
+    a = np.concatenate([g.uniform(0, 100, 3000), [4.0, 9.0, 0.0, 5.0, 1e-30, 3.0e30]]).astype(np.float32)
+    w = np.concatenate([g.uniform(0, 0.5, 3000), [1.0, 1.0, 2.0, 0.0, 1e-30, 1e-30]]).astype(np.float32)
+    lam, mult = oracle.smooth_factors(a, w)
+    assert lam[-6] == 2.0 and lam[-5] == 3.0 and lam[-4] == 1.0 and lam[-3] == 1.0 and lam[-2] == 1.0
+    for k in range(a.size):
+        if a[k] == 0 or w[k] == 0:
+            assert lam[k] == 1.0 and mult[k] == 1.0
+            continue
+        q = F(float(a[k])) / F(float(w[k]))
+        lo, hi = _fp32_neighbours(lam[k])
+        # lambda is the nearest fp32 to sqrt(q): q lies between the squares of the midpoints
+        assert (F(float(lo)) + F(float(lam[k]))) ** 2 / 4 <= q <= (F(float(hi)) + F(float(lam[k]))) ** 2 / 4, k
+        assert mult[k] == float(exact.fp32(1 / F(float(lam[k])))), k
+
+
+def test_smooth_act_exact_and_torch():
+    g = inputs.rng(52)
+    x = inputs.bf16_bits_to_f32(inputs.to_bf16_bits(g.standard_normal((7, 64)).astype(np.float32) * 3))
+    mult = g.uniform(0.01, 20, 64).astype(np.float32)
+    got = oracle.smooth_act(x, mult)
+    bf16_max = F(2 ** 8 - 1, 2 ** 7) * 2 ** 127
+    for m in range(x.shape[0]):
+        for k in range(x.shape[1]):
+            p = exact.fp32(F(float(x[m, k])) * F(float(mult[k])))
+            assert got[m, k] == float(exact.round_format(p, 7, -126, bf16_max)), (m, k)
+    want = (torch.from_numpy(x) * torch.from_numpy(mult)).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(got, want)
+    # a power-of-two multiplier only moves the exponent of a bf16 value
+    assert np.array_equal(oracle.smooth_act(x, np.full(64, 0.25, np.float32)), x * np.float32(0.25))
