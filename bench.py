@@ -217,9 +217,12 @@ def main():
             for M in (1, 4, 16):
                 xm = xb[:M].contiguous()
                 ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(GEMV_COPIES)]
-                def run(copies=copies, xm=xm, ys=ys, g=g):
+                wsb = nv.workspace_bytes(nv.OP_GEMV_W4A16, M, N)   # split-K partials (M > 4, short weights)
+                gws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+
+                def run(copies=copies, xm=xm, ys=ys, g=g, gws=gws):
                     for (cc, ss), y in zip(copies, ys):
-                        nv.gemv_w4a16(xm, cc, ss, g, out=y)
+                        nv.gemv_w4a16(xm, cc, ss, g, out=y, workspace=gws, split_k=gws is not None)
 
                 nbytes = GEMV_COPIES * (N * K * 0.5625 + 2 * M * K + 2 * M * N)
                 capture(f"gemv_{N}x{K}_M{M}", run, nbytes=nbytes, flops=GEMV_COPIES * 2.0 * M * N * K,
@@ -259,8 +262,11 @@ def main():
             ad, hd = bf16(aa), bf16(hh)
             Ms = aa.shape[0]
             w = {name: nv.quantize_mse(f32(x)) for name, x in inputs.dit_weights(stream_id)}
-            ws_a = torch.empty(nv.workspace_bytes(nv.OP_GEMM_W4A4, Ms, ad.shape[1]), dtype=torch.uint8, device=dev)
-            ws_h = torch.empty(nv.workspace_bytes(nv.OP_GEMM_W4A4, Ms, hd.shape[1]), dtype=torch.uint8, device=dev)
+            # workspaces with room for split-K partial sums (used by the short text-stream products)
+            ws_a = torch.empty(max(nv.gemm_workspace_bytes(Ms, w[name][0].shape[0], ad.shape[1])
+                                   for name in ("to_q", "to_k", "to_v", "mlp_up")), dtype=torch.uint8, device=dev)
+            ws_h = torch.empty(nv.gemm_workspace_bytes(Ms, w["mlp_down"][0].shape[0], hd.shape[1]), dtype=torch.uint8,
+                               device=dev)
             outs = {name: torch.empty((Ms, w[name][0].shape[0]), dtype=torch.bfloat16, device=dev) for name in w}
             dit_calls.append((ad, hd, w, ws_a, ws_h, outs))
         dit_flops = 0.0

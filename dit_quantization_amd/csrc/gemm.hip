@@ -316,11 +316,17 @@ __device__ __forceinline__ void buffer_to_lds2(__amdgpu_buffer_rsrc_t buf, uint3
 // LORA: the epilogue adds L lora_up^T (bf16 L [M, rank] from
 // act_quant_lora_kernel, bf16 lora_up [N, rank]) with
 // v_mfma_f32_32x32x16_bf16 after scaling the product by s_gA s_gW.
-template <int BM, int BN, int WM, int WN, bool LORA>
+// SPLIT (short activations, never with LORA): workgroup b computes K range
+// b % splits of tile b / splits and stores its unscaled fp32 sums in
+// partial [splits, M, N]; gemm_splitk_reduce_kernel finishes the product.
+// (A separate instantiation: folding the range offsets into the unsplit
+// kernel cost it 3-5 % on the prefill and DiT shapes.)
+template <int BM, int BN, int WM, int WN, bool LORA, bool SPLIT>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu((BM / WM) * (BN / WN) >= 128 * 128 ? 1 : 2))) void gemm_w4a4_kernel(
     const uint16_t* __restrict__ a_hat, const float* __restrict__ sga_ptr, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ sgw_ptr, int M, int N, int K, void* __restrict__ y,
-    int bf16_out, const uint16_t* __restrict__ lora_l, const uint16_t* __restrict__ lora_up, int rank) {
+    int bf16_out, const uint16_t* __restrict__ lora_l, const uint16_t* __restrict__ lora_up, int rank, int splits,
+    float* __restrict__ partial) {
   constexpr int NT = WM * WN * 64;                       // threads
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;    // 32x32 tiles per wave
   constexpr int A_CHUNKS = BM * BK * 2 / 16;             // 16-byte chunks per A stage
@@ -341,8 +347,9 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu((B
   // tiles, which then share A rows / W rows in that XCD's L2.
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const int ntiles = tiles_m * tiles_n;
-  int bid = blockIdx.x;
-  if ((ntiles & 7) == 0) {  // a bijection on [0, ntiles) when 8 divides it
+  const int split = SPLIT ? (int)(blockIdx.x % splits) : 0;
+  int bid = SPLIT ? (int)(blockIdx.x / splits) : (int)blockIdx.x;
+  if (!SPLIT && (ntiles & 7) == 0) {  // a bijection on [0, ntiles) when 8 divides it
     const int per_xcd = ntiles >> 3;
     bid = (bid & 7) * per_xcd + (bid >> 3);
   }
@@ -359,7 +366,9 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu((B
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int l32 = lane & 31, g = lane >> 5;  // MFMA row/col and k lane group
-  const int KT = K / BK;
+  const int kts = SPLIT ? (K / BK + splits - 1) / splits : K / BK;
+  const int kt0 = SPLIT ? split * kts : 0;            // first K step of this workgroup's range
+  const int KT = SPLIT ? min(kts, K / BK - kt0) : kts;  // K steps in the range (>= 1)
 
   // ---- DMA sources.  A: instruction j of wave w fills slots
   // [64 (w APT + j), +64); slot S holds row S / 8, 16-byte chunk
@@ -386,7 +395,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu((B
   }
 
   auto dma = [&](Stage& stg, int kt) {
-    const uint32_t k = (uint32_t)min(kt, KT - 1);
+    const uint32_t k = (uint32_t)(kt0 + min(kt, KT - 1));
 #pragma unroll
     for (int j = 0; j < APT; ++j) buffer_to_lds16(abuf, stg.a + 64 * (wave * APT + j), a_off[j], k * (BK * 2));
 #pragma unroll
@@ -559,6 +568,10 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu((B
       for (int r = 0; r < 16; ++r) {
         const int m = m0 + wm * (BM / WM) + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
         if (m >= M) continue;
+        if (SPLIT) {
+          partial[((int64_t)split * M + m) * N + n] = acc[i][t][r];
+          continue;
+        }
         float v = LORA ? acc[i][t][r] : acc[i][t][r] * alpha;
         if (bf16_out)
           reinterpret_cast<uint16_t*>(y)[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_bits(v);
@@ -569,26 +582,76 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu((B
   }
 }
 
+// y = round(fp32(s_gA s_gW) * (((p_0 + p_1) + ...) + p_{S-1})) per element.
+__global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(const float* __restrict__ partial, int splits,
+                                                                 int64_t n, const float* __restrict__ sga_ptr,
+                                                                 const float* __restrict__ sgw_ptr,
+                                                                 void* __restrict__ y, int bf16_out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = partial[i];
+  for (int t = 1; t < splits; ++t) s += partial[t * n + i];
+  const float v = s * ((*sga_ptr) * (*sgw_ptr));
+  if (bf16_out)
+    reinterpret_cast<uint16_t*>(y)[i] = (uint16_t)f32_to_bf16_bits(v);
+  else
+    reinterpret_cast<float*>(y)[i] = v;
+}
+
+namespace {
+int64_t tiles128(int64_t M, int64_t N) { return ((M + 127) / 128) * ((N + 127) / 128); }
+int64_t tiles256(int64_t M, int64_t N) { return ((M + 255) / 256) * ((N + 255) / 256); }
+}  // namespace
+
+int gemm_max_splits(int64_t M, int64_t N) {
+  // Short activations with fewer 128 x 128 tiles than CUs: enough K ranges
+  // for about 384 workgroups, at most 8.
+  if (M == 0 || N == 0 || tiles256(M, N) >= 128) return 1;
+  const int64_t t = tiles128(M, N);
+  if (t >= 256) return 1;
+  const int64_t s = (384 + t - 1) / t;
+  return (int)(s > 8 ? 8 : s);
+}
+
+int gemm_splits(int64_t M, int64_t N, int64_t K) {
+  int s = gemm_max_splits(M, N);
+  const int64_t kt = K / 64;
+  if (s > kt / 32) s = (int)(kt / 32);  // at least 32 K steps per range (shorter ranges lost to the extra pass)
+  if (s <= 1) return 1;
+  const int64_t kts = (kt + s - 1) / s;
+  return (int)((kt + kts - 1) / kts);  // no empty range
+}
+
 hipError_t launch_gemm_w4a4(const uint16_t* a_hat, const float* sga, const uint8_t* codes, const uint8_t* scales,
                             const float* sgw, int64_t M, int64_t N, int64_t K, void* y, bool bf16_out,
-                            const uint16_t* lora_l, const uint16_t* lora_up, int rank, hipStream_t stream) {
+                            const uint16_t* lora_l, const uint16_t* lora_up, int rank, float* partial,
+                            hipStream_t stream) {
   // 256 x 256 tiles (8 waves, 128 x 64 per wave) whenever they cover at least
   // half of the 256 CUs; otherwise 128 x 128 tiles (4 waves) for more
-  // parallelism on short activations (measured on the prefill and DiT shapes).
+  // parallelism on short activations (measured on the prefill and DiT shapes),
+  // split along K when the caller's workspace holds the partial sums.
   const int b = bf16_out ? 1 : 0;
-  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
-#define NVFP4_GEMM(BM, BN, WM, WN, L, T)                                                                       \
-  hipLaunchKernelGGL((gemm_w4a4_kernel<BM, BN, WM, WN, L>), dim3((unsigned)(T)), dim3(WM * WN * 64), 0, stream, \
-                     a_hat, sga, codes, scales, sgw, (int)M, (int)N, (int)K, y, b, lora_l, lora_up, rank)
+  const int64_t t256 = tiles256(M, N);
+  const int64_t t128 = tiles128(M, N);
+  const int splits = (rank == 0 && partial) ? gemm_splits(M, N, K) : 1;
+#define NVFP4_GEMM(BM, BN, WM, WN, L, S, T)                                                                      \
+  hipLaunchKernelGGL((gemm_w4a4_kernel<BM, BN, WM, WN, L, S>), dim3((unsigned)(T)), dim3(WM * WN * 64), 0, stream, \
+                     a_hat, sga, codes, scales, sgw, (int)M, (int)N, (int)K, y, b, lora_l, lora_up, rank, splits,   \
+                     partial)
   if (t256 >= 128) {
-    if (rank > 0) NVFP4_GEMM(256, 256, 2, 4, true, t256);
-    else NVFP4_GEMM(256, 256, 2, 4, false, t256);
+    if (rank > 0) NVFP4_GEMM(256, 256, 2, 4, true, false, t256);
+    else NVFP4_GEMM(256, 256, 2, 4, false, false, t256);
   } else {
-    if (rank > 0) NVFP4_GEMM(128, 128, 2, 2, true, t128);
-    else NVFP4_GEMM(128, 128, 2, 2, false, t128);
+    if (rank > 0) NVFP4_GEMM(128, 128, 2, 2, true, false, t128);
+    else if (splits > 1) NVFP4_GEMM(128, 128, 2, 2, false, true, t128 * splits);
+    else NVFP4_GEMM(128, 128, 2, 2, false, false, t128);
   }
 #undef NVFP4_GEMM
+  if (splits > 1) {
+    const int64_t n = M * N;
+    hipLaunchKernelGGL(gemm_splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, partial,
+                       splits, n, sga, sgw, y, b);
+  }
   return hipGetLastError();
 }
 

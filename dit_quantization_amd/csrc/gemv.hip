@@ -74,21 +74,26 @@ __device__ __forceinline__ void scale_pairs(u32x2 d, int lane, uint32_t pair[4])
   }
 }
 
-// grid: ceil(N / (16 T)) workgroups of NW waves.  DENSE: the M > 4 operand
-// layout; otherwise staggered (M <= 4).
-template <int DENSE, int T, int NW>
+// grid: ceil(N / (16 T)) workgroups of NW waves (times `splits` with
+// SPLIT).  DENSE: the M > 4 operand layout; otherwise staggered (M <= 4).
+// SPLIT: workgroup b takes super-chunk range b % splits of row block
+// b / splits and stores its unscaled fp32 sums in partial [splits, M, N]
+// (gemv_splitk_reduce_kernel adds them in range order).
+template <int DENSE, int T, int NW, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) void gemv_w4a16_kernel(const uint16_t* __restrict__ x,
                                                              const uint8_t* __restrict__ codes,
                                                              const uint8_t* __restrict__ scales,
                                                              const float* __restrict__ sg_ptr, int M, int N, int K,
-                                                             int bf16_out, void* __restrict__ out) {
+                                                             int bf16_out, void* __restrict__ out, int splits,
+                                                             float* __restrict__ partial) {
   constexpr int SW = 4;              // super-chunks per pass (one 8-byte scale load per lane)
   constexpr int XL = DENSE ? 4 : 1;  // x loads per super-chunk
   __shared__ f32x4 red[NW][T][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nl = lane & 15, g = lane >> 4;
-  const int n0 = blockIdx.x * (16 * T);
+  const int split = SPLIT ? (int)(blockIdx.x % splits) : 0;
+  const int n0 = (SPLIT ? (int)(blockIdx.x / splits) : (int)blockIdx.x) * (16 * T);
   const int rows = min(16 * T, N - n0);
   const int half = K / 2, sbytes = K / 16;
   const __amdgpu_buffer_rsrc_t cbuf = make_buf(codes + (int64_t)n0 * half, (uint32_t)(rows * half));
@@ -96,8 +101,10 @@ __global__ __launch_bounds__(NW * 64) void gemv_w4a16_kernel(const uint16_t* __r
   const __amdgpu_buffer_rsrc_t xbuf = make_buf(x, (uint32_t)(M * K * 2));
   const int nch = K / 32;
   const int nsc = (nch + 3) / 4;
-  const int per = (nsc + NW - 1) / NW;
-  const int sbeg = wave * per, send = min(sbeg + per, nsc);
+  const int sps = SPLIT ? (nsc + splits - 1) / splits : nsc;  // super-chunks of this workgroup's range
+  const int r0 = split * sps, r1 = min(r0 + sps, nsc);
+  const int per = (r1 - r0 + NW - 1) / NW;
+  const int sbeg = r0 + wave * per, send = min(sbeg + per, r1);
   // x role: dense lane (m, g) holds row m; staggered lane (4 j + i, g) holds
   // row i for MFMA j = jx.
   const int xm = DENSE ? nl : (nl & 3);
@@ -198,7 +205,9 @@ __global__ __launch_bounds__(NW * 64) void gemv_w4a16_kernel(const uint16_t* __r
     for (int i = 0; i < (DENSE ? 4 : 1); ++i) {
       const int m = DENSE ? 4 * (l >> 4) + i : (l >> 4);
       if (m < M && n < N) {
-        if (bf16_out)
+        if (SPLIT)
+          partial[((int64_t)split * M + m) * N + n] = sum[i];
+        else if (bf16_out)
           reinterpret_cast<uint16_t*>(out)[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_bits(sum[i] * sg);
         else
           reinterpret_cast<float*>(out)[(int64_t)m * N + n] = sum[i] * sg;
@@ -349,8 +358,43 @@ __global__ __launch_bounds__(256) void gemv_m1_kernel(const uint16_t* __restrict
   }
 }
 
+// y = round(s_g * (((p_0 + p_1) + ...) + p_{S-1})) per element.
+__global__ __launch_bounds__(256) void gemv_splitk_reduce_kernel(const float* __restrict__ partial, int splits,
+                                                                 int64_t n, const float* __restrict__ sg_ptr,
+                                                                 void* __restrict__ y, int bf16_out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = partial[i];
+  for (int t = 1; t < splits; ++t) s += partial[t * n + i];
+  const float v = s * (*sg_ptr);
+  if (bf16_out)
+    reinterpret_cast<uint16_t*>(y)[i] = (uint16_t)f32_to_bf16_bits(v);
+  else
+    reinterpret_cast<float*>(y)[i] = v;
+}
+
+int gemv_max_splits(int64_t M, int64_t N) {
+  // M > 4 on weights with fewer than 8192 rows: 64-row blocks, about 256
+  // workgroups in all (x is read once per workgroup, so the rows per
+  // workgroup, not the K range, set its L2 traffic).
+  if (M <= 4 || M > 16 || N >= 8192 || N == 0) return 1;
+  const int64_t blocks = (N + 63) / 64;
+  const int64_t s = (256 + blocks - 1) / blocks;
+  return (int)(s > 8 ? 8 : s);
+}
+
+int gemv_splits(int64_t M, int64_t N, int64_t K) {
+  int s = gemv_max_splits(M, N);
+  const int64_t nsc = (K / 32 + 3) / 4;
+  if (K < 8192 || s > nsc / 16) s = (int)(K < 8192 ? 1 : nsc / 16);  // long rows only, >= 16 super-chunks a range
+  if (s <= 1) return 1;
+  const int64_t sps = (nsc + s - 1) / s;
+  return (int)((nsc + sps - 1) / sps);
+}
+
 hipError_t launch_gemv_w4a16(const uint16_t* x, const uint8_t* codes, const uint8_t* scales, const float* sg,
-                             int64_t M, int64_t N, int64_t K, void* y, bool bf16_out, hipStream_t stream) {
+                             int64_t M, int64_t N, int64_t K, void* y, bool bf16_out, float* partial,
+                             hipStream_t stream) {
   int b = bf16_out ? 1 : 0;
   const int64_t nch = K / 32;                      // 16-byte code chunks per row
   if (M == 1 && nch <= 4 * 64 * 4) {
@@ -365,14 +409,27 @@ hipError_t launch_gemv_w4a16(const uint16_t* x, const uint8_t* codes, const uint
   }
   // M > 1: MFMA kernels.  32 rows per workgroup when that still gives at
   // least one workgroup per CU (256), else 16; 16 waves split long rows.
+  // M > 4 on tall weights: 64 rows per workgroup, so each x fragment feeds 4
+  // row tiles (x is read from L2 once per workgroup; measured on the
+  // 14336 x 4096 decode shape at M = 16: 15.0 us against 17.1 us with 32 rows).
   const int dense = M > 4 ? 1 : 0;
   const bool t2 = N >= 32 * 256;
   const bool nw16 = !t2 && K >= 8192;
 #define NVFP4_GEMV_MFMA(D, T, NW)                                                                                 \
-  hipLaunchKernelGGL((gemv_w4a16_kernel<D, T, NW>), dim3((unsigned)((N + 16 * T - 1) / (16 * T))), dim3(NW * 64), \
-                     0, stream, x, codes, scales, sg, (int)M, (int)N, (int)K, b, y)
+  hipLaunchKernelGGL((gemv_w4a16_kernel<D, T, NW, false>), dim3((unsigned)((N + 16 * T - 1) / (16 * T))),         \
+                     dim3(NW * 64), 0, stream, x, codes, scales, sg, (int)M, (int)N, (int)K, b, y, 1, nullptr)
+  const int splits = partial ? gemv_splits(M, N, K) : 1;
+  if (splits > 1) {
+    // 64-row blocks, each split into `splits` K ranges, then the ordered sum.
+    hipLaunchKernelGGL((gemv_w4a16_kernel<1, 4, 8, true>), dim3((unsigned)(((N + 63) / 64) * splits)), dim3(512), 0,
+                       stream, x, codes, scales, sg, (int)M, (int)N, (int)K, b, y, splits, partial);
+    const int64_t n = M * N;
+    hipLaunchKernelGGL(gemv_splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, partial,
+                       splits, n, sg, y, b);
+    return hipGetLastError();
+  }
   if (dense) {
-    if (t2) NVFP4_GEMV_MFMA(1, 2, 8);
+    if (t2) NVFP4_GEMV_MFMA(1, 4, 8);
     else if (nw16) NVFP4_GEMV_MFMA(1, 1, 16);
     else NVFP4_GEMV_MFMA(1, 1, 8);
   } else {

@@ -28,8 +28,13 @@ hipError_t launch_quantize_search(const void* x, bool bf16, bool four_over_six, 
                                   uint8_t* codes, uint8_t* scales, hipStream_t stream);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* sg, int64_t n_elems,
                           void* out, bool bf16_out, hipStream_t stream);
+// Split-K of the M > 4 decode product on short weights (partial: fp32
+// [gemv_splits(M, N, K), M, N] scratch, or nullptr for no split).
+int gemv_max_splits(int64_t M, int64_t N);
+int gemv_splits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemv_w4a16(const uint16_t* x, const uint8_t* codes, const uint8_t* scales, const float* sg,
-                             int64_t M, int64_t N, int64_t K, void* y, bool bf16_out, hipStream_t stream);
+                             int64_t M, int64_t N, int64_t K, void* y, bool bf16_out, float* partial,
+                             hipStream_t stream);
 hipError_t launch_act_quant_f16(const uint16_t* a, int64_t n_elems, const float* sg, uint16_t* a_hat,
                                 hipStream_t stream);
 // K ranges the fused activation-quantization + LoRA-down pass splits each
@@ -39,8 +44,14 @@ int lora_splits(int64_t M, int64_t K);
 hipError_t launch_act_quant_lora(const uint16_t* a, const float* sg, const uint16_t* down, int rank, int64_t M,
                                  int64_t K, const float* mult, uint16_t* a_hat, uint16_t* lora_l, float* partial,
                                  hipStream_t stream);
+// Split-K of the W4A4 product (short activations): the most K ranges any K
+// can get for an M x N output, and the count used for a given K.
+int gemm_max_splits(int64_t M, int64_t N);
+int gemm_splits(int64_t M, int64_t N, int64_t K);
+// partial: fp32 [gemm_splits(M, N, K), M, N] scratch, or nullptr (no split).
 hipError_t launch_gemm_w4a4(const uint16_t* a_hat, const float* sga, const uint8_t* codes, const uint8_t* scales,
                             const float* sgw, int64_t M, int64_t N, int64_t K, void* y, bool bf16_out,
-                            const uint16_t* lora_l, const uint16_t* lora_up, int rank, hipStream_t stream);
+                            const uint16_t* lora_l, const uint16_t* lora_up, int rank, float* partial,
+                            hipStream_t stream);
 
 }  // namespace nvfp4

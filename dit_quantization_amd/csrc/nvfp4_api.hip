@@ -11,7 +11,7 @@ namespace {
 
 using namespace nvfp4;
 
-constexpr int kVersion = 1 * 10000 + 4 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 5 * 100 + 0;
 static_assert(kSweepCandidates == NVFP4_SWEEP_CANDIDATES, "candidate count of the activation scale sweep");
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -139,9 +139,18 @@ int gemm_common(const void* a, const float* a_global, const uint8_t* w_codes, co
              : launch_act_quant_f16(ab, M * K, sga, a_hat, s);
     if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
   }
+  // Split-K partial sums (plain product on short activations) when the
+  // workspace extends past the regions above by their size.
+  float* split_partial = nullptr;
+  if (!lora) {
+    const int splits = gemm_splits(M, N, K);
+    const size_t base = gemm_ws_bytes(M, K);
+    if (splits > 1 && ws_bytes >= base + (size_t)splits * M * N * 4)
+      split_partial = reinterpret_cast<float*>(ws + base);
+  }
   return launch_status(launch_gemm_w4a4(a_hat, sga, w_codes, w_scales, w_global, M, N, K, y,
                                         y_dtype == NVFP4_BF16, lora ? lora_l : nullptr,
-                                        reinterpret_cast<const uint16_t*>(lora_up), rank, s));
+                                        reinterpret_cast<const uint16_t*>(lora_up), rank, split_partial, s));
 }
 
 }  // namespace
@@ -171,9 +180,16 @@ size_t nvfp4_workspace_bytes(int op, int64_t a, int64_t b) {
     case NVFP4_OP_QUANTIZE: return amax_ws_bytes(a * b, false) > amax_ws_bytes(a * b, true)
                                        ? amax_ws_bytes(a * b, false) : amax_ws_bytes(a * b, true);
     case NVFP4_OP_GEMM_W4A4: return gemm_ws_bytes(a, b);
-    case NVFP4_OP_GEMV_W4A16: return 0;
+    case NVFP4_OP_GEMV_W4A16: {
+      const int s = gemv_max_splits(a, b);
+      return s > 1 ? round256((size_t)s * a * b * 4) : 0;
+    }
     case NVFP4_OP_GEMM_W4A4_LORA: return gemm_lora_ws_bytes(a, b);
     case NVFP4_OP_ACT_CALIBRATE: return calibrate_ws_bytes(a * b);
+    case NVFP4_OP_GEMM_W4A4_SPLITK: {
+      const int s = gemm_max_splits(a, b);
+      return s > 1 ? round256((size_t)s * a * b * 4) : 0;
+    }
     default: return 0;
   }
 }
@@ -221,13 +237,17 @@ int nvfp4_gemv_w4a16(const void* x, const uint8_t* w_codes, const uint8_t* w_sca
   if (!aligned(x, 16) || !aligned(w_codes, 16) || !aligned(w_scales, 4) || !aligned(w_global, 4) ||
       !aligned(y, 4))
     return NVFP4_ERR_ALIGN;
+  if (workspace && !aligned(workspace, 256)) return NVFP4_ERR_ALIGN;
   if (M == 0 || N == 0) return NVFP4_OK;
   if (K == 0) return NVFP4_ERR_UNSUPPORTED;
-  (void)workspace;
-  (void)ws_bytes;
+  // Split-K partial sums when the workspace holds them.
+  const int splits = gemv_splits(M, N, K);
+  float* partial = (splits > 1 && workspace && ws_bytes >= (size_t)splits * M * N * 4)
+                       ? reinterpret_cast<float*>(workspace) : nullptr;
   clear_error();
   return launch_status(launch_gemv_w4a16(reinterpret_cast<const uint16_t*>(x), w_codes, w_scales, w_global, M, N,
-                                         K, y, y_dtype == NVFP4_BF16, reinterpret_cast<hipStream_t>(stream)));
+                                         K, y, y_dtype == NVFP4_BF16, partial,
+                                         reinterpret_cast<hipStream_t>(stream)));
 }
 
 int nvfp4_gemm_w4a4(const void* a, const float* a_global, const uint8_t* w_codes, const uint8_t* w_scales,

@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_LAUNCH, ERR_FLAGS = range(9)
 F32, BF16 = 0, 1
 GLOBAL_COMPUTE, GLOBAL_GIVEN = 0, 1
-OP_QUANTIZE, OP_GEMM_W4A4, OP_GEMV_W4A16, OP_GEMM_W4A4_LORA, OP_ACT_CALIBRATE = 0, 1, 2, 3, 4
+OP_QUANTIZE, OP_GEMM_W4A4, OP_GEMV_W4A16, OP_GEMM_W4A4_LORA, OP_ACT_CALIBRATE, OP_GEMM_W4A4_SPLITK = (
+    0, 1, 2, 3, 4, 5)
 SWEEP_CANDIDATES = 17
 GEMM_QUANTIZE_ACT, GEMM_REUSE_ACT = 0, 1
 
@@ -177,8 +178,11 @@ def _check_weight(codes, scales, K):
     return N
 
 
-def gemv_w4a16(x, w_codes, w_scales, w_global, out_dtype=torch.bfloat16, workspace=None, out=None):
-    """y = x W^T for bf16 x [M, K] (M <= 16) and NVFP4 weights [N, K]."""
+def gemv_w4a16(x, w_codes, w_scales, w_global, out_dtype=torch.bfloat16, workspace=None, out=None, split_k=True):
+    """y = x W^T for bf16 x [M, K] (M <= 16) and NVFP4 weights [N, K].
+
+    split_k=False (with no workspace given) runs the unsplit kernel even where
+    the library would split K."""
     _need_cuda(x, w_codes, w_scales, w_global)
     if x.dtype != torch.bfloat16 or x.dim() != 2:
         raise ValueError("x must be a 2-D bfloat16 tensor")
@@ -186,7 +190,10 @@ def gemv_w4a16(x, w_codes, w_scales, w_global, out_dtype=torch.bfloat16, workspa
     N = _check_weight(w_codes, w_scales, K)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=x.device)
-    ws = workspace if workspace is not None else _alloc_ws(workspace_bytes(OP_GEMV_W4A16, M, N), x.device)
+    if workspace is not None or not split_k:
+        ws = workspace
+    else:
+        ws = _alloc_ws(workspace_bytes(OP_GEMV_W4A16, M, N), x.device)
     st = lib().nvfp4_gemv_w4a16(_ptr(x), _ptr(w_codes), _ptr(w_scales), _ptr(w_global), M, N, K, _ptr(out),
                                 _dtype_code(out.dtype), _ptr(ws), 0 if ws is None else ws.numel(), _stream())
     _check("nvfp4_gemv_w4a16", st)
@@ -220,7 +227,7 @@ def gemm_w4a4(a, w_codes, w_scales, w_global, a_global=None, out_dtype=torch.bfl
     if smooth is not None and lora is None:
         raise ValueError("smooth needs the low-rank factors (lora=)")
     if lora is None:
-        ws = workspace if workspace is not None else _alloc_ws(workspace_bytes(OP_GEMM_W4A4, M, K), a.device)
+        ws = workspace if workspace is not None else _alloc_ws(gemm_workspace_bytes(M, N, K), a.device)
         st = lib().nvfp4_gemm_w4a4(_ptr(a), _ptr(a_global), _ptr(w_codes), _ptr(w_scales), _ptr(w_global), M, N, K,
                                    _ptr(out), _dtype_code(out.dtype), flags, _ptr(ws), ws.numel(), _stream())
         _check("nvfp4_gemm_w4a4", st)
@@ -247,6 +254,12 @@ def gemm_w4a4(a, w_codes, w_scales, w_global, a_global=None, out_dtype=torch.bfl
                                     _dtype_code(out.dtype), flags, _ptr(ws), ws.numel(), _stream())
     _check("nvfp4_gemm_w4a4_svdq", st)
     return out
+
+
+def gemm_workspace_bytes(M, N, K, split_k=True):
+    """Workspace of the plain W4A4 product; with split_k also the partial sums
+    that let short activations split K."""
+    return workspace_bytes(OP_GEMM_W4A4, M, K) + (workspace_bytes(OP_GEMM_W4A4_SPLITK, M, N) if split_k else 0)
 
 
 def gemm_workspace_layout(M, K):

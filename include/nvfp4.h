@@ -79,7 +79,8 @@ enum {
   NVFP4_OP_GEMM_W4A4 = 1,
   NVFP4_OP_GEMV_W4A16 = 2,
   NVFP4_OP_GEMM_W4A4_LORA = 3,
-  NVFP4_OP_ACT_CALIBRATE = 4
+  NVFP4_OP_ACT_CALIBRATE = 4,
+  NVFP4_OP_GEMM_W4A4_SPLITK = 5
 };
 
 /* number of candidate scales of nvfp4_act_scale_sweep */
@@ -156,9 +157,12 @@ int nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const float* glob
  *   y[m, n] = s_gW * sum_k x[m, k] * q[n, k] * s_b[n, k/16]
  *   x        [M, K] bf16;  w_codes [N, K/2];  w_scales [N, K/16];
  *   w_global 1 device fp32; y [M, N] of y_dtype (NVFP4_BF16 or NVFP4_F32)
- *   workspace reserved: this version needs none
- *            (nvfp4_workspace_bytes(NVFP4_OP_GEMV_W4A16, M, N) returns 0);
- *            may be NULL
+ *   workspace optional: with at least nvfp4_workspace_bytes(
+ *            NVFP4_OP_GEMV_W4A16, M, N) bytes (256-byte aligned), products
+ *            with M > 4, N < 8192 and K >= 8192 cut K into up to 8 ranges
+ *            whose fp32 sums are added in range order (reproducible; they may
+ *            differ from the unsplit sum by fp32 rounding); NULL or a smaller
+ *            workspace: no split (the size is 0 for shapes never split)
  *   0 <= M <= 16 (the decode batch; M = 0 or N = 0 is a no-op); K % 32 == 0
  *   and 0 < K <= 2^24, otherwise NVFP4_ERR_UNSUPPORTED.  fp32 accumulation,
  *   fp32 epilogue (x s_gW), round-to-nearest-even bf16 output.
@@ -194,6 +198,12 @@ int nvfp4_gemv_w4a16(const void* x, const uint8_t* w_codes, const uint8_t* w_sca
  *            and `a_global` are not read.
  *   y[m, n] = round(fp32(s_gA * s_gW) * sum_k (q_a s_a)[m,k] (q_w s_w)[n,k])
  *   with the products exact and the sum accumulated in fp32.
+ *   Split-K: when the output has few tiles (short activations) and the
+ *   workspace is at least nvfp4_workspace_bytes(NVFP4_OP_GEMM_W4A4, M, K) +
+ *   nvfp4_workspace_bytes(NVFP4_OP_GEMM_W4A4_SPLITK, M, N) bytes, K is cut
+ *   into up to 8 ranges whose fp32 sums are added in range order (a fixed
+ *   order, so results are reproducible; they may differ from the unsplit sum
+ *   by fp32 rounding).  With a smaller workspace the product is not split.
  */
 int nvfp4_gemm_w4a4(const void* a, const float* a_global, const uint8_t* w_codes,
                     const uint8_t* w_scales, const float* w_global,
@@ -318,8 +328,10 @@ int nvfp4_act_scale_sweep(const void* x, int64_t rows, int64_t cols, const float
 
 /* Workspace size in bytes for an operation: NVFP4_OP_QUANTIZE and
  * NVFP4_OP_ACT_CALIBRATE with (rows, cols), NVFP4_OP_GEMM_W4A4 and
- * NVFP4_OP_GEMM_W4A4_LORA with (M, K), NVFP4_OP_GEMV_W4A16 with (M, N); 0 for
- * an unknown op or negative sizes. */
+ * NVFP4_OP_GEMM_W4A4_LORA with (M, K), NVFP4_OP_GEMV_W4A16 and
+ * NVFP4_OP_GEMM_W4A4_SPLITK (the optional split-K extra of nvfp4_gemm_w4a4,
+ * 0 when that output is never split) with (M, N); 0 for an unknown op or
+ * negative sizes. */
 size_t nvfp4_workspace_bytes(int op, int64_t rows_or_m, int64_t cols_or_k);
 
 /* Static, NUL-terminated description of a status code. */

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert nv.lib().nvfp4_version() == 10400
+    assert nv.lib().nvfp4_version() == 10500
     for s in range(9):
         assert nv.status_string(s) and nv.status_string(s) != "unknown status"
     assert nv.status_string(99) == "unknown status"
@@ -42,7 +42,9 @@ def test_workspace_sizes():
     assert nv.workspace_bytes(nv.OP_QUANTIZE, 4096, 4096) >= 4 * 1 and nv.workspace_bytes(nv.OP_QUANTIZE, 4096, 4096) % 256 == 0
     g = nv.workspace_bytes(nv.OP_GEMM_W4A4, 4096, 4096)
     assert g >= 256 + 2 * 4096 * 4096
-    assert nv.workspace_bytes(nv.OP_GEMV_W4A16, 16, 4096) == 0
+    assert nv.workspace_bytes(nv.OP_GEMV_W4A16, 16, 4096) == 4 * 16 * 4096 * 4   # optional split-K partials
+    assert nv.workspace_bytes(nv.OP_GEMV_W4A16, 4, 4096) == 0
+    assert nv.workspace_bytes(nv.OP_GEMV_W4A16, 16, 14336) == 0
     # the low-rank variant adds L (bf16 [M, 128] at most) after the quantized activation
     # (and, for short activations, fp32 partial sums of the split down projection)
     assert nv.workspace_bytes(nv.OP_GEMM_W4A4_LORA, 4096, 4096) >= g + 2 * 4096 * 128
@@ -50,6 +52,11 @@ def test_workspace_sizes():
     assert nv.workspace_bytes(nv.OP_GEMM_W4A4_LORA, 16384, 1024) == g16 + 2 * 16384 * 128
     assert nv.gemm_lora_l_offset(100, 64) == 256 + 12800
     assert nv.workspace_bytes(99, 1, 1) == 0
+    # split-K partials: only for outputs with few tiles (at most 8 ranges)
+    assert nv.workspace_bytes(nv.OP_GEMM_W4A4_SPLITK, 4096, 14336) == 0
+    assert nv.workspace_bytes(nv.OP_GEMM_W4A4_SPLITK, 512, 12288) == 0
+    assert nv.workspace_bytes(nv.OP_GEMM_W4A4_SPLITK, 512, 3072) == 4 * 512 * 3072 * 4
+    assert nv.workspace_bytes(nv.OP_GEMM_W4A4_SPLITK, 1, 64) == 8 * 64 * 4
     assert nv.workspace_bytes(nv.OP_QUANTIZE, -1, 16) == 0
 
 
@@ -94,6 +101,7 @@ def test_gemv_validation():
     assert f(A16 + 2, A16, A16, A4, 1, 64, 64, A16, nv.BF16, None, 0, None) == nv.ERR_ALIGN
     assert f(A16, A16, A16, A4, 1, 64, (1 << 24) + 32, A16, nv.BF16, None, 0, None) == nv.ERR_UNSUPPORTED
     assert f(A16, A16, A16, A4, 0, 64, 64, A16, nv.BF16, None, 0, None) == nv.OK      # empty: no launch
+    assert f(A16, A16, A16, A4, 8, 64, 64, A16, nv.BF16, A16 + 16, 1 << 20, None) == nv.ERR_ALIGN
 
 
 def test_gemm_validation():

@@ -49,6 +49,28 @@ def test_gemv_ragged(shape, M):
     assert_bracket_bf16(yb.reshape(-1), ystar, tau, "bf16")
 
 
+@pytest.mark.parametrize("shape", [(300, 8320), (1000, 16384), (64, 8192)])
+@pytest.mark.parametrize("M", [5, 16])
+def test_gemv_splitk(shape, M):
+    """M > 4 on short weights with long rows splits K (3 uneven ranges of
+    17, 17, 17, 14 super-chunks for K = 8320; 8 for K = 16384; 4 for 64 rows):
+    the split and the unsplit product both meet tau, the split one repeats."""
+    N, K = shape
+    print(f"[case] gemv split-K N={N} K={K} M={M}", flush=True)
+    assert nv.workspace_bytes(nv.OP_GEMV_W4A16, M, N) > 0
+    w = inputs.student_t_f32((N, K), N + K + 1)
+    xb = inputs.gemv_x(K, M)
+    c, s, g = _quant_weight(w, oracle.MSE)
+    ystar, tau = oracle.dot_w4a16(inputs.bf16_bits_to_f32(xb), host(c), host(s), float(host(g)[0]))
+    xd = dev_bf16(xb)
+    y_split = host(nv.gemv_w4a16(xd, c, s, g, out_dtype=torch.float32))
+    y_plain = host(nv.gemv_w4a16(xd, c, s, g, out_dtype=torch.float32, split_k=False))
+    assert_within_tau(y_split.reshape(-1), ystar, tau, "split fp32")
+    assert_within_tau(y_plain.reshape(-1), ystar, tau, "plain fp32")
+    assert_bracket_bf16(host(nv.gemv_w4a16(xd, c, s, g)).reshape(-1), ystar, tau, "split bf16")
+    assert np.array_equal(host(nv.gemv_w4a16(xd, c, s, g, out_dtype=torch.float32)), y_split)
+
+
 @pytest.mark.parametrize("which", [0, 1])
 def test_gemv_decode_full_size(which):
     w = inputs.gemv_weights()[which]
@@ -145,6 +167,42 @@ def test_gemm_dit_block_sampled():
             M, N = act.shape[0], w.shape[0]
             _check_gemm(act, c, s, g, pairs=_sample_pairs(M, N, 600, stream * 10 + len(name)),
                         what=f"dit stream{stream} {name}")
+
+
+@pytest.mark.parametrize("mnk", [(70, 130, 1024), (300, 520, 4096), (33, 96, 4096), (100, 200, 1344),
+                                 (512, 3072, 3072)])
+def test_gemm_splitk_matches_oracle(mnk):
+    """Short activations split K over workgroups when the workspace holds the
+    partial sums; both the split and the unsplit product must meet tau, and
+    the split one must repeat bit for bit."""
+    M, N, K = mnk
+    print(f"[case] gemm split-K M={M} N={N} K={K}", flush=True)
+    assert nv.workspace_bytes(nv.OP_GEMM_W4A4_SPLITK, M, N) > 0
+    a = inputs.normal_f32((M, K), M + 31)
+    a, _ = inputs.with_outlier_columns(a, max(1, K // 100), 32)
+    ab = inputs.to_bf16_bits(a)
+    c, s, g = _quant_weight(inputs.student_t_f32((N, K), N + 33), oracle.MSE)
+    a_dev = dev_bf16(ab)
+    ws_split = torch.empty(nv.gemm_workspace_bytes(M, N, K), dtype=torch.uint8, device=DEV)
+    ws_plain = torch.empty(nv.gemm_workspace_bytes(M, N, K, split_k=False), dtype=torch.uint8, device=DEV)
+    y_split = nv.gemm_w4a4(a_dev, c, s, g, out_dtype=torch.float32, workspace=ws_split)
+    y_plain = nv.gemm_w4a4(a_dev, c, s, g, out_dtype=torch.float32, workspace=ws_plain)
+    yb_split = nv.gemm_w4a4(a_dev, c, s, g, workspace=ws_split)
+    torch.cuda.synchronize()
+    ac, as_, asg = oracle.quantize(inputs.bf16_bits_to_f32(ab), oracle.ABSMAX)
+    oc, os_, og = host(c), host(s), float(host(g)[0])
+    if M * N > 200000:
+        pairs = _sample_pairs(M, N, 4000, 5)
+        ystar, tau = oracle.dot_w4a4(ac, as_, asg, oc, os_, og, K, pairs=pairs, M=M, N=N)
+        sel = (pairs[0], pairs[1])
+    else:
+        ystar, tau = oracle.dot_w4a4(ac, as_, asg, oc, os_, og, K)
+        sel = slice(None)
+    assert_within_tau(host(y_split)[sel].reshape(-1), ystar, tau, "split fp32")
+    assert_within_tau(host(y_plain)[sel].reshape(-1), ystar, tau, "plain fp32")
+    assert_bracket_bf16(host(yb_split)[sel].reshape(-1), ystar, tau, "split bf16")
+    y_again = nv.gemm_w4a4(a_dev, c, s, g, out_dtype=torch.float32, workspace=ws_split)
+    assert np.array_equal(host(y_again), host(y_split))
 
 
 def test_gemm_and_gemv_deterministic():
