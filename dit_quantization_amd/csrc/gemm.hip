@@ -305,7 +305,7 @@ __device__ __forceinline__ void buffer_to_lds2(__amdgpu_buffer_rsrc_t buf, uint3
 //    lane fetches the 16-byte chunk that belongs in its LDS slot under an
 //    XOR swizzle (conflict-free 16-byte fragment reads).
 //  * packed weights: row r's 32 code bytes of the step sit in two 16-byte
-//    slots, swapped for rows with bit 2 set (conflict-free reads); the 4
+//    slots, swapped for rows with bit 3 set (conflict-free reads); the 4
 //    scale bytes of a row are contiguous.
 // One barrier per step, after an explicit wait for this step's stage.  Each
 // lane reads its weight chunk and scales once per step and unpacks 8 codes
@@ -372,16 +372,19 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu((B
 
   // ---- DMA sources.  A: instruction j of wave w fills slots
   // [64 (w APT + j), +64); slot S holds row S / 8, 16-byte chunk
-  // (S % 8) ^ (row % 8) of the step's 64 k.
+  // (S % 8) ^ ((row / 2) % 8) of the step's 64 k.  A 16-byte LDS read serves
+  // 16 lanes (16 consecutive rows) at a time: rows 2j and 2j + 1 fall in the
+  // two halves of the 64 banks and the 8 row pairs get 8 different chunks
+  // (with the swizzle on row % 8, rows r and r + 8 collided: 2-way conflicts).
   const __amdgpu_buffer_rsrc_t abuf = make_buf(a_hat + (int64_t)m0 * K, (uint32_t)(min(BM, M - m0) * K * 2));
   uint32_t a_off[APT];
 #pragma unroll
   for (int j = 0; j < APT; ++j) {
     const int S = 64 * (wave * APT + j) + lane;
-    const int r = S >> 3, c = (S & 7) ^ (r & 7);
+    const int r = S >> 3, c = (S & 7) ^ ((r >> 1) & 7);
     a_off[j] = (uint32_t)((r * K + 8 * c) * 2);
   }
-  // W codes: slot u (= tid + NT j) holds row u / 2, half (u % 2) ^ ((row >> 2) & 1).
+  // W codes: slot u (= tid + NT j) holds row u / 2, half (u % 2) ^ ((row >> 3) & 1).
   // Scales: dword slot u holds bytes 2 (u % 2) .. +2 of row u / 2.
   const int w_rows = min(BN, N - n0);
   const __amdgpu_buffer_rsrc_t wbuf = make_buf(codes + (int64_t)n0 * (K / 2), (uint32_t)(w_rows * (K / 2)));
@@ -390,7 +393,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu((B
 #pragma unroll
   for (int j = 0; j < WPT; ++j) {
     const int u = tid + NT * j;
-    w_off[j] = (uint32_t)((u >> 1) * (K / 2) + 16 * ((u & 1) ^ ((u >> 3) & 1)));
+    w_off[j] = (uint32_t)((u >> 1) * (K / 2) + 16 * ((u & 1) ^ ((u >> 4) & 1)));
     s_off[j] = (uint32_t)((u >> 1) * (K / 16) + 2 * (u & 1));
   }
 
@@ -419,12 +422,12 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu((B
   int a_row8[TM];
 #pragma unroll
   for (int i = 0; i < TM; ++i) a_row8[i] = (wm * (BM / WM) + 32 * i + l32) * 8;
-  const int a_sw = l32 & 7;
+  const int a_sw = (l32 >> 1) & 7;
   int w_slot[TN], s_slot[TN];
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
     const int rw = wn * (BN / WN) + 32 * t + l32;
-    w_slot[t] = 2 * rw + (g ^ ((rw >> 2) & 1));
+    w_slot[t] = 2 * rw + (g ^ ((rw >> 3) & 1));
     s_slot[t] = 2 * rw + g;
   }
 
