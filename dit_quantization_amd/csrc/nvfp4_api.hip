@@ -103,9 +103,11 @@ int gemm_common(const void* a, const float* a_global, const uint8_t* w_codes, co
   if (y_dtype != NVFP4_F32 && y_dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
   if (M < 0 || N < 0 || K < 0 || rank < 0 || !mul_ok(M, K) || !mul_ok(N, K) || !mul_ok(M, N)) return NVFP4_ERR_SHAPE;
   if (K % 16 != 0) return NVFP4_ERR_SHAPE;
-  if (K % 64 != 0 || K == 0 || M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > (int64_t)1 << 30)
+  // K <= 2^22: a 256-row operand panel (256 K 2 bytes) and its DMA offsets
+  // stay within the 32-bit buffer ranges the kernels address.
+  if (K % 64 != 0 || K == 0 || M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > (int64_t)1 << 22)
     return NVFP4_ERR_UNSUPPORTED;
-  if (lora && (rank % 16 != 0 || rank > kMaxLoraRank || K > (int64_t)1 << 22)) return NVFP4_ERR_UNSUPPORTED;
+  if (lora && (rank % 16 != 0 || rank > kMaxLoraRank)) return NVFP4_ERR_UNSUPPORTED;
   if ((!reuse && !aligned(a, 16)) || !aligned(w_codes, 16) || !aligned(w_scales, 4) || !aligned(w_global, 4) ||
       (a_global && !aligned(a_global, 4)) || !aligned(y, 16) || !aligned(workspace, 256))
     return NVFP4_ERR_ALIGN;

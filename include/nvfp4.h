@@ -181,8 +181,9 @@ int nvfp4_gemv_w4a16(const void* x, const uint8_t* w_codes, const uint8_t* w_sca
  *            otherwise a device fp32 used as s_gA (a static activation scale)
  *   w_codes [N, K/2], w_scales [N, K/16], w_global: the NVFP4 weight
  *   y        [M, N] of y_dtype (NVFP4_BF16 or NVFP4_F32)
- *   K % 64 == 0 (one K step of the kernel; all configured shapes qualify),
- *   otherwise NVFP4_ERR_UNSUPPORTED.
+ *   K % 64 == 0 (one K step of the kernel; all configured shapes qualify)
+ *   and K <= 2^22 (32-bit addressing of a 256-row operand panel),
+ *   otherwise NVFP4_ERR_UNSUPPORTED; M, N <= 2^30.
  *   workspace >= nvfp4_workspace_bytes(NVFP4_OP_GEMM_W4A4, M, K) bytes,
  *            256-byte aligned.  On return it holds, at fixed offsets:
  *              [0, 4)       s_gA (fp32)

@@ -115,6 +115,8 @@ def test_gemm_validation():
     assert f(A16, None, A16, A16, A4, 64, 64, 64, A16, nv.BF16, 6, A16, W, None) == nv.ERR_FLAGS
     assert f(A16, None, A16, A16, A4, 64, 64, 40, A16, nv.BF16, Q, A16, W, None) == nv.ERR_SHAPE
     assert f(A16, None, A16, A16, A4, 64, 64, 96, A16, nv.BF16, Q, A16, W, None) == nv.ERR_UNSUPPORTED
+    # K beyond 2^22 would overflow the 32-bit addressing of a 256-row panel
+    assert f(A16, None, A16, A16, A4, 64, 64, (1 << 22) + 64, A16, nv.BF16, Q, A16, 1 << 40, None) == nv.ERR_UNSUPPORTED
     assert f(A16, None, A16, A16, A4, 64, 64, 64, A16, nv.BF16, Q, A16 + 16, W, None) == nv.ERR_ALIGN
     assert f(A16, None, A16, A16, A4, 64, 64, 64, A16, nv.BF16, Q, A16, 16, None) == nv.ERR_WORKSPACE
     assert f(A16, None, A16, A16, A4, 0, 64, 64, A16, nv.BF16, Q, A16, W, None) == nv.OK

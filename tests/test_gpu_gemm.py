@@ -15,16 +15,28 @@ pytestmark = pytest.mark.gpu
 
 
 def _quant_weight(w, method=oracle.ABSMAX):
-    fn = nv.quantize_absmax if method == oracle.ABSMAX else nv.quantize_mse
-    c, s, g = fn(dev_f32(w))
-    return c, s, g
+    """The oracle's NVFP4 encoding of w, uploaded: the products' weight inputs
+    come from the oracle, never from the GPU quantizer."""
+    c, s, g = oracle.quantize(w, method)
+    dev = (torch.from_numpy(c).to(DEV), torch.from_numpy(s).to(DEV),
+           torch.tensor([g], dtype=torch.float32, device=DEV))
+    _ORACLE_WEIGHTS[dev[0].data_ptr()] = (c, s, g)
+    return dev
+
+
+_ORACLE_WEIGHTS = {}   # device codes pointer -> the oracle's (codes, scales, s_g) it was uploaded from
+
+
+def _oracle_weight(c):
+    return _ORACLE_WEIGHTS[c.data_ptr()]
 
 
 def test_tiny_config_gemv():
     w, xb = inputs.tiny()
+    gc, gs, _ = nv.quantize_absmax(dev_f32(w))      # the GPU quantizer on the tiny config ...
     c, s, g = _quant_weight(w)
-    oc, os_, og = oracle.quantize(w)
-    assert np.array_equal(host(c), oc) and np.array_equal(host(s), os_)
+    oc, os_, og = _oracle_weight(c)
+    assert np.array_equal(host(gc), oc) and np.array_equal(host(gs), os_)   # ... matches the oracle's encoding
     x = inputs.bf16_bits_to_f32(xb)
     ystar, tau = oracle.dot_w4a16(x, oc, os_, og)
     yb = host(nv.gemv_w4a16(dev_bf16(xb), c, s, g))
@@ -41,7 +53,7 @@ def test_gemv_ragged(shape, M):
     w = inputs.student_t_f32((N, K), N + K)
     xb = inputs.gemv_x(K, M)
     c, s, g = _quant_weight(w, oracle.MSE)
-    oc, os_, og = host(c), host(s), float(host(g)[0])
+    oc, os_, og = _oracle_weight(c)
     ystar, tau = oracle.dot_w4a16(inputs.bf16_bits_to_f32(xb), oc, os_, og)
     y32 = host(nv.gemv_w4a16(dev_bf16(xb), c, s, g, out_dtype=torch.float32))
     assert_within_tau(y32.reshape(-1), ystar, tau, "fp32")
@@ -60,8 +72,9 @@ def test_gemv_splitk(shape, M):
     assert nv.workspace_bytes(nv.OP_GEMV_W4A16, M, N) > 0
     w = inputs.student_t_f32((N, K), N + K + 1)
     xb = inputs.gemv_x(K, M)
-    c, s, g = _quant_weight(w, oracle.MSE)
-    ystar, tau = oracle.dot_w4a16(inputs.bf16_bits_to_f32(xb), host(c), host(s), float(host(g)[0]))
+    oc, os_, og = oracle.quantize(w, oracle.MSE if N * K <= 1 << 22 else oracle.ABSMAX)
+    c, s, g = torch.from_numpy(oc).to(DEV), torch.from_numpy(os_).to(DEV), torch.tensor([og], device=DEV)
+    ystar, tau = oracle.dot_w4a16(inputs.bf16_bits_to_f32(xb), oc, os_, og)
     xd = dev_bf16(xb)
     y_split = host(nv.gemv_w4a16(xd, c, s, g, out_dtype=torch.float32))
     y_plain = host(nv.gemv_w4a16(xd, c, s, g, out_dtype=torch.float32, split_k=False))
@@ -76,10 +89,10 @@ def test_gemv_decode_full_size(which):
     w = inputs.gemv_weights()[which]
     N, K = w.shape
     print(f"[case] gemv full N={N} K={K}", flush=True)
-    c, s, g = _quant_weight(w)
+    c, s, g = nv.quantize_absmax(dev_f32(w))
     oc, os_, og = oracle.quantize(w)
     assert float(host(g)[0]) == og
-    assert np.array_equal(host(s), os_) and np.array_equal(host(c), oc)   # full-size absmax parity
+    assert np.array_equal(host(s), os_) and np.array_equal(host(c), oc)   # full-size absmax parity (so c, s, g are the oracle's)
     xb = inputs.gemv_x(K, 16)
     x = inputs.bf16_bits_to_f32(xb)
     ystar, tau = oracle.dot_w4a16(x, oc, os_, og)
@@ -111,7 +124,7 @@ def _check_gemm(ab, w_c, w_s, w_g, pairs=None, a_global=None, what=""):
     want = oracle.dequant(ac, as_, 1.0, M, K)
     assert np.array_equal(ahat, want), np.argwhere(ahat != want)[:5]
     # products
-    oc, os_, og = host(w_c), host(w_s), float(host(w_g)[0])
+    oc, os_, og = _oracle_weight(w_c)
     if pairs is None:
         ystar, tau = oracle.dot_w4a4(ac, as_, asg, oc, os_, og, K)
         sel = slice(None)
@@ -154,7 +167,7 @@ def _sample_pairs(M, N, n, seed):
 def test_gemm_prefill_full_size_sampled():
     ab = inputs.prefill_activation()
     (_, w), = list(inputs.layerset(["gate"]))
-    c, s, g = _quant_weight(w, oracle.MSE)
+    c, s, g = _quant_weight(w)
     _check_gemm(ab, c, s, g, pairs=_sample_pairs(4096, 14336, 3000, 1), what="prefill")
 
 
@@ -162,7 +175,7 @@ def test_gemm_dit_block_sampled():
     a_img, a_txt, h_img, h_txt = inputs.dit_activations()
     for stream, (a, h) in enumerate(((a_img, h_img), (a_txt, h_txt))):
         for name, w in inputs.dit_weights(stream):
-            c, s, g = _quant_weight(w, oracle.MSE)
+            c, s, g = _quant_weight(w)
             act = h if name == "mlp_down" else a
             M, N = act.shape[0], w.shape[0]
             _check_gemm(act, c, s, g, pairs=_sample_pairs(M, N, 600, stream * 10 + len(name)),
@@ -181,7 +194,7 @@ def test_gemm_splitk_matches_oracle(mnk):
     a = inputs.normal_f32((M, K), M + 31)
     a, _ = inputs.with_outlier_columns(a, max(1, K // 100), 32)
     ab = inputs.to_bf16_bits(a)
-    c, s, g = _quant_weight(inputs.student_t_f32((N, K), N + 33), oracle.MSE)
+    c, s, g = _quant_weight(inputs.student_t_f32((N, K), N + 33), oracle.MSE if N * K <= 1 << 22 else oracle.ABSMAX)
     a_dev = dev_bf16(ab)
     ws_split = torch.empty(nv.gemm_workspace_bytes(M, N, K), dtype=torch.uint8, device=DEV)
     ws_plain = torch.empty(nv.gemm_workspace_bytes(M, N, K, split_k=False), dtype=torch.uint8, device=DEV)
@@ -190,7 +203,7 @@ def test_gemm_splitk_matches_oracle(mnk):
     yb_split = nv.gemm_w4a4(a_dev, c, s, g, workspace=ws_split)
     torch.cuda.synchronize()
     ac, as_, asg = oracle.quantize(inputs.bf16_bits_to_f32(ab), oracle.ABSMAX)
-    oc, os_, og = host(c), host(s), float(host(g)[0])
+    oc, os_, og = _oracle_weight(c)
     if M * N > 200000:
         pairs = _sample_pairs(M, N, 4000, 5)
         ystar, tau = oracle.dot_w4a4(ac, as_, asg, oc, os_, og, K, pairs=pairs, M=M, N=N)
@@ -214,3 +227,37 @@ def test_gemm_and_gemv_deterministic():
     v1 = host(nv.gemv_w4a16(dev_bf16(ab[:16]), c, s, g))
     v2 = host(nv.gemv_w4a16(dev_bf16(ab[:16]), c, s, g))
     assert np.array_equal(v1, v2)
+
+
+@pytest.mark.parametrize("M", [1, 5])
+def test_gemv_maximum_k(M):
+    """K = 2^24, the largest the decode product accepts (N = 16 rows; M = 5 also
+    splits K into 8 ranges)."""
+    N, K = 16, 1 << 24
+    print(f"[case] gemv max K N={N} K={K} M={M}", flush=True)
+    w = inputs.normal_f32((N, K), 77, std=0.02)
+    c, s, g = _quant_weight(w)
+    del w
+    oc, os_, og = _oracle_weight(c)
+    xb = inputs.gemv_x(K, M)
+    ystar, tau = oracle.dot_w4a16(inputs.bf16_bits_to_f32(xb), oc, os_, og)
+    y32 = host(nv.gemv_w4a16(dev_bf16(xb), c, s, g, out_dtype=torch.float32))
+    assert_within_tau(y32.reshape(-1), ystar, tau, "max K fp32")
+
+
+def test_gemm_maximum_k():
+    """K = 2^22, the largest the W4A4 product accepts (M = N = 16), split into
+    8 K ranges and unsplit."""
+    M, N, K = 16, 16, 1 << 22
+    print(f"[case] gemm max K M={M} N={N} K={K}", flush=True)
+    ab = inputs.to_bf16_bits(inputs.normal_f32((M, K), 78))
+    c, s, g = _quant_weight(inputs.normal_f32((N, K), 79, std=0.02))
+    oc, os_, og = _oracle_weight(c)
+    ac, as_, asg = oracle.quantize(inputs.bf16_bits_to_f32(ab), oracle.ABSMAX)
+    ystar, tau = oracle.dot_w4a4(ac, as_, asg, oc, os_, og, K)
+    del ac, as_
+    a_dev = dev_bf16(ab)
+    for split in (True, False):
+        ws = torch.empty(nv.gemm_workspace_bytes(M, N, K, split_k=split), dtype=torch.uint8, device=DEV)
+        y32 = host(nv.gemm_w4a4(a_dev, c, s, g, out_dtype=torch.float32, workspace=ws))
+        assert_within_tau(y32.reshape(-1), ystar, tau, f"max K split={split}")

@@ -14,20 +14,23 @@ import torch
 import oracle
 from dit_quantization_amd import inputs
 from dit_quantization_amd import nvfp4 as nv
-from tests.gpu_helpers import DEV, assert_bracket_bf16, assert_within_tau, dev_bf16, dev_f32, host
+from tests.gpu_helpers import DEV, assert_bracket_bf16, assert_within_tau, dev_bf16, host
 
 pytestmark = pytest.mark.gpu
 
 
-def _quant_weight(w):
-    return nv.quantize_mse(dev_f32(w))
+def _quant_weight(w, method=oracle.MSE):
+    """The oracle's NVFP4 encoding of w: (device tensors, host arrays)."""
+    c, s, g = oracle.quantize(w, method)
+    return (torch.from_numpy(c).to(DEV), torch.from_numpy(s).to(DEV),
+            torch.tensor([g], dtype=torch.float32, device=DEV)), (c, s, g)
 
 
-def _check_lora(ab, w, down_b, up_b, pairs=None, a_global=None, what=""):
+def _check_lora(ab, w, down_b, up_b, pairs=None, a_global=None, what="", method=oracle.MSE):
     M, K = ab.shape
     N, r = up_b.shape
     print(f"[case] gemm+lora {what} M={M} N={N} K={K} r={r}", flush=True)
-    c, s, g = _quant_weight(w)
+    (c, s, g), (oc, os_, og) = _quant_weight(w, method)
     ws = torch.empty(nv.workspace_bytes(nv.OP_GEMM_W4A4_LORA, M, K), dtype=torch.uint8, device=DEV)
     a_dev, down, up = dev_bf16(ab), dev_bf16(down_b), dev_bf16(up_b)
     ag = None if a_global is None else torch.tensor([a_global], dtype=torch.float32, device=DEV)
@@ -47,7 +50,6 @@ def _check_lora(ab, w, down_b, up_b, pairs=None, a_global=None, what=""):
     lstar, ltau = oracle.lora_term(a32, d32, np.eye(r, dtype=np.float32))
     assert_within_tau(inputs.bf16_bits_to_f32(L).reshape(-1), lstar, ltau, what + " L")
     # products
-    oc, os_, og = host(c), host(s), float(host(g)[0])
     if pairs is None:
         ystar, tau = oracle.dot_w4a4(ac, as_, asg, oc, os_, og, K)
         lst, lt = oracle.lora_term(a32, d32, u32)
@@ -108,13 +110,14 @@ def test_lora_dit_block_sampled(stream):
         M, K = act.shape
         N = w.shape[0]
         down, up = inputs.lora_factors(32, K, N, 200 + 10 * stream + i)
-        _check_lora(act, w, down, up, pairs=_sample_pairs(M, N, 600, 50 + i), what=f"dit stream{stream} {name}")
+        _check_lora(act, w, down, up, pairs=_sample_pairs(M, N, 600, 50 + i), what=f"dit stream{stream} {name}",
+                    method=oracle.ABSMAX)
 
 
 def test_lora_rank_zero_branch_equals_plain():
     """A zero up-projection leaves exactly the plain W4A4 product."""
     ab = inputs.to_bf16_bits(inputs.normal_f32((200, 512), 3))
-    c, s, g = _quant_weight(inputs.student_t_f32((320, 512), 4))
+    (c, s, g), _ = _quant_weight(inputs.student_t_f32((320, 512), 4))
     down, _ = inputs.lora_factors(32, 512, 320, 5)
     up = torch.zeros((320, 32), dtype=torch.bfloat16, device=DEV)
     a = dev_bf16(ab)

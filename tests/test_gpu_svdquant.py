@@ -20,40 +20,61 @@ from tests.gpu_helpers import DEV, assert_bracket_bf16, assert_within_tau, dev_b
 pytestmark = pytest.mark.gpu
 
 
-def _layer(M, N, K, rank, seed, outliers=True):
+def _inputs(M, N, K, seed, outliers=True):
     a = inputs.normal_f32((M, K), seed)
     if outliers:
         a, _ = inputs.with_outlier_columns(a, max(1, K // 100), seed + 1)
     ab = inputs.to_bf16_bits(a)
     w = inputs.student_t_f32((N, K), seed + 2)
-    act_amax = torch.zeros(K, dtype=torch.float32, device=DEV)
-    nv.channel_amax(dev_bf16(ab), act_amax)
-    layer = svdquant.prepare(w, host(act_amax), rank)
-    return ab, w, layer
+    return ab, w
+
+
+def _layer(M, N, K, rank, seed, outliers=True):
+    """A prepared SVDQuant layer (GPU-quantized residual), for the property tests."""
+    ab, w = _inputs(M, N, K, seed, outliers)
+    act_amax = np.abs(inputs.bf16_bits_to_f32(ab)).max(axis=0)
+    return ab, w, svdquant.prepare(w, act_amax, rank)
+
+
+def _oracle_layer(ab, w, rank):
+    """The same split with every parity input from the oracle or the seeded
+    inputs: the oracle's smoothing multipliers (asserted equal to the host
+    preparation's), the host SVD factors, and the oracle's MSE encoding of the
+    residual, uploaded.  Returns (device layer, host factors, oracle codes)."""
+    x32 = inputs.bf16_bits_to_f32(ab)
+    act_amax = np.abs(x32).max(axis=0)
+    f = svdquant.factors(w, act_amax, rank)
+    lam, mult = oracle.smooth_factors(act_amax, np.abs(w).max(axis=0))
+    assert np.array_equal(f["smooth"], mult) and np.array_equal(f["lam"], lam)
+    oc, os_, og = oracle.quantize(f["residual"], oracle.MSE)
+    layer = {"smooth": torch.from_numpy(mult).to(DEV), "down": dev_bf16(f["down"]), "up": dev_bf16(f["up"]),
+             "codes": torch.from_numpy(oc).to(DEV), "scales": torch.from_numpy(os_).to(DEV),
+             "global": torch.tensor([og], dtype=torch.float32, device=DEV)}
+    return layer, f, (oc, os_, og), mult
 
 
 @pytest.mark.parametrize("mnkr", [(70, 130, 192, 16), (200, 320, 512, 32), (33, 96, 1024, 48)])
 def test_svdq_parity(mnkr):
     M, N, K, r = mnkr
     print(f"[case] svdq M={M} N={N} K={K} r={r}", flush=True)
-    ab, w, layer = _layer(M, N, K, r, 700 + M)
+    ab, w = _inputs(M, N, K, 700 + M)
+    layer, f, (oc, os_, og), mult = _oracle_layer(ab, w, r)
     a_dev = dev_bf16(ab)
     ws = torch.empty(nv.workspace_bytes(nv.OP_GEMM_W4A4_LORA, M, K), dtype=torch.uint8, device=DEV)
     y32 = svdquant.forward(a_dev, layer, out_dtype=torch.float32, workspace=ws)
     torch.cuda.synchronize()
-    xs = oracle.smooth_act(inputs.bf16_bits_to_f32(ab), host(layer["smooth"]))
+    xs = oracle.smooth_act(inputs.bf16_bits_to_f32(ab), mult)
     wsh = host(ws)
     ac, as_, asg = oracle.quantize(xs, oracle.ABSMAX)
     assert wsh[:4].view(np.float32)[0] == np.float32(asg)
     ahat = wsh[256:256 + 2 * M * K].view(np.float16).reshape(M, K).astype(np.float32)
     assert np.array_equal(ahat, oracle.dequant(ac, as_, 1.0, M, K))
-    down = inputs.bf16_bits_to_f32(host(layer["down"]))
-    up = inputs.bf16_bits_to_f32(host(layer["up"]))
+    down = inputs.bf16_bits_to_f32(f["down"])
+    up = inputs.bf16_bits_to_f32(f["up"])
     off = nv.gemm_lora_l_offset(M, K)
     L = wsh[off:off + 2 * M * r].view(np.uint16).reshape(M, r)
     lstar, ltau = oracle.lora_term(xs, down, np.eye(r, dtype=np.float32))
     assert_within_tau(inputs.bf16_bits_to_f32(L).reshape(-1), lstar, ltau, "L")
-    oc, os_, og = host(layer["codes"]), host(layer["scales"]), float(host(layer["global"])[0])
     ystar, tau = oracle.dot_w4a4(ac, as_, asg, oc, os_, og, K)
     lst, lt = oracle.lora_term(xs, down, up)
     assert_within_tau(host(y32).reshape(-1), ystar + lst, tau + lt, "fp32")
@@ -63,12 +84,13 @@ def test_svdq_parity(mnkr):
 
 def test_svdq_static_scale():
     M, N, K, r = 96, 128, 256, 16
-    ab, w, layer = _layer(M, N, K, r, 800)
+    ab, w = _inputs(M, N, K, 800)
+    layer, _, _, mult = _oracle_layer(ab, w, r)
     ws = torch.empty(nv.workspace_bytes(nv.OP_GEMM_W4A4_LORA, M, K), dtype=torch.uint8, device=DEV)
     ag = torch.tensor([0.004], dtype=torch.float32, device=DEV)
     svdquant.forward(dev_bf16(ab), layer, workspace=ws, a_global=ag)
     torch.cuda.synchronize()
-    xs = oracle.smooth_act(inputs.bf16_bits_to_f32(ab), host(layer["smooth"]))
+    xs = oracle.smooth_act(inputs.bf16_bits_to_f32(ab), mult)
     ac, as_, _ = oracle.quantize(xs, oracle.ABSMAX, sg=0.004)
     ahat = host(ws)[256:256 + 2 * M * K].view(np.float16).reshape(M, K).astype(np.float32)
     assert np.array_equal(ahat, oracle.dequant(ac, as_, 1.0, M, K))
