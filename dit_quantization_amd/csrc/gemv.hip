@@ -25,7 +25,9 @@
 // Rows past N, chunks past K and x rows past M are buffer loads at an
 // out-of-range offset, which return zero without a memory access.  Waves
 // are added in LDS in wave order; the epilogue multiplies by s_g and rounds
-// to bf16 (RNE).
+// to bf16 (RNE).  Workgroups of 16 (or 32 / 64 rows on tall weights) read x
+// from L2 once each; M > 4 on short weights with long rows splits K over
+// workgroups instead (partial sums added in range order by a second pass).
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -407,11 +409,11 @@ hipError_t launch_gemv_w4a16(const uint16_t* x, const uint8_t* codes, const uint
 #undef NVFP4_GEMV_M1
     return hipGetLastError();
   }
-  // M > 1: MFMA kernels.  32 rows per workgroup when that still gives at
-  // least one workgroup per CU (256), else 16; 16 waves split long rows.
-  // M > 4 on tall weights: 64 rows per workgroup, so each x fragment feeds 4
-  // row tiles (x is read from L2 once per workgroup; measured on the
-  // 14336 x 4096 decode shape at M = 16: 15.0 us against 17.1 us with 32 rows).
+  // M > 1: MFMA kernels.  On weights of at least 8192 rows, 32 rows per
+  // workgroup (M <= 4) or 64 (M > 4: each x fragment then feeds 4 row tiles,
+  // and x is read from L2 once per workgroup; 14336 x 4096 at M = 16: 15.0 us
+  // against 17.1 us with 32 rows); else 16 rows, with 16 waves splitting
+  // rows of K >= 8192 (unless the split-K path above took the call).
   const int dense = M > 4 ? 1 : 0;
   const bool t2 = N >= 32 * 256;
   const bool nw16 = !t2 && K >= 8192;
