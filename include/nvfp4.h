@@ -1,6 +1,14 @@
 /*
- * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 library: block quantizer,
- * dequantizer, W4A16 decode GEMV and W4A4 GEMM.
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 library:
+ *   - block quantizers: nvfp4_quantize_absmax, nvfp4_quantize_mse,
+ *     nvfp4_quantize_4o6 (four-over-six), and nvfp4_dequant;
+ *   - W4A16 decode product: nvfp4_gemv_w4a16;
+ *   - W4A4 product with per-call activation quantization: nvfp4_gemm_w4a4,
+ *     with a fused 16-bit low-rank (LoRA) branch: nvfp4_gemm_w4a4_lora, and
+ *     on an SVDQuant-smoothed input: nvfp4_gemm_w4a4_svdq;
+ *   - calibration of a static activation scale: nvfp4_act_amax,
+ *     nvfp4_act_scale_sweep, and per-channel ranges: nvfp4_channel_amax;
+ *   - nvfp4_workspace_bytes, nvfp4_status_string, nvfp4_version.
  *
  * Format (from the pages "Tu pipeline NVFP4: meter 62 GB de modelo en 24 GB de
  * laptop", section 2 "Que es realmente NVFP4", and "NVFP4 en difusion: la
