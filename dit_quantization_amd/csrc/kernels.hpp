@@ -24,8 +24,10 @@ hipError_t launch_act_scale_sweep(const uint16_t* x, int64_t n_elems, const floa
                                   double* errors, float* scale, hipStream_t stream);
 hipError_t launch_quantize_absmax(const void* x, bool bf16, int64_t n_elems, const float* sg, uint8_t* codes,
                                   uint8_t* scales, hipStream_t stream);
-hipError_t launch_quantize_search(const void* x, bool bf16, bool four_over_six, int64_t n_elems, const float* sg,
-                                  uint8_t* codes, uint8_t* scales, hipStream_t stream);
+hipError_t launch_quantize_4o6(const void* x, bool bf16, int64_t n_elems, const float* sg, uint8_t* codes,
+                               uint8_t* scales, hipStream_t stream);
+hipError_t launch_quantize_mse(const void* x, bool bf16, int64_t n_elems, const float* sg, uint8_t* codes,
+                               uint8_t* scales, hipStream_t stream);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* sg, int64_t n_elems,
                           void* out, bool bf16_out, hipStream_t stream);
 // Split-K of the M > 4 decode product on short weights (partial: fp32

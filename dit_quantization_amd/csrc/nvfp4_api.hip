@@ -61,9 +61,9 @@ int quantize_common(Search mode, const void* x, int x_dtype, int64_t rows, int64
     hipError_t e = launch_global_scale(x, bf16, n, reinterpret_cast<float*>(ws), gs, s);
     if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
   }
-  hipError_t e = mode == Search::kAbsmax
-                     ? launch_quantize_absmax(x, bf16, n, gs, codes, scales, s)
-                     : launch_quantize_search(x, bf16, mode == Search::kFourOverSix, n, gs, codes, scales, s);
+  hipError_t e = mode == Search::kAbsmax        ? launch_quantize_absmax(x, bf16, n, gs, codes, scales, s)
+                 : mode == Search::kFourOverSix ? launch_quantize_4o6(x, bf16, n, gs, codes, scales, s)
+                                                : launch_quantize_mse(x, bf16, n, gs, codes, scales, s);
   return launch_status(e);
 }
 

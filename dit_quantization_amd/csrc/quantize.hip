@@ -231,6 +231,102 @@ __global__ __launch_bounds__(256) void quantize_absmax_kernel(const void* __rest
   }
 }
 
+// Four-over-six block scales ("Tu pipeline NVFP4 ...", section 2, algorithm
+// table: each block chooses 6 or 4 as the value its maximum maps to, by
+// reconstruction error), in the absmax pass's layout: one lane per half
+// block, lanes 2b and 2b+1 share block b, so every load is coalesced.  The
+// two candidates are the nearest E4M3 values to max / (6 s_g) (the absmax
+// scale) and max / (4 s_g).  A candidate's error is
+// E = ((d_0^2 + d_1^2) + ...) + d_15^2 in fp64 with d_e = |W_e| - c s_g |q_e|
+// rounded once: the even lane sums its 8 terms, the odd lane continues that
+// sum with its own 8 in element order, and picks the max -> 4 scale only on a
+// strictly smaller error.
+template <bool kBF16>
+__global__ __launch_bounds__(256) void quantize_4o6_kernel(const void* __restrict__ x, int64_t n_half,
+                                                           const float* __restrict__ sg_ptr,
+                                                           uint32_t* __restrict__ codes,
+                                                           uint8_t* __restrict__ scales) {
+  const float sg = *sg_ptr;
+  const float inv_sg = 1.0f / sg;
+  const double sg64 = (double)sg;
+  const bool pack = (reinterpret_cast<uintptr_t>(scales) & 3) == 0;
+  const bool odd = (threadIdx.x & 1) != 0;
+  int64_t stride = (int64_t)gridDim.x * blockDim.x;  // a multiple of 64
+  for (int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; h < n_half; h += stride) {
+    float w[8];
+    load8<kBF16>(x, h, w);
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(w[j]));
+    m = fmaxf(m, __shfl_xor(m, 1));
+    const uint32_t k6 = e4m3_code_rne((double)m / (6.0 * sg64));
+    const uint32_t k4 = e4m3_code_rne((double)m / (4.0 * sg64));  // >= k6
+    const float c6 = e4m3_to_f32(k6), c4 = e4m3_to_f32(k4);
+    const uint32_t word6 = encode8(w, c6, sg, inv_sg);
+    uint32_t word = word6, sc = k6;
+    if (k4 != k6) {  // the lane pair agrees (same m)
+      const uint32_t word4 = encode8(w, c4, sg, inv_sg);
+      const double cs6 = (double)c6 * sg64, cs4 = (double)c4 * sg64;  // exact
+      float q6[8], q4[8];
+      fp4x8_to_f32(word6, q6);
+      fp4x8_to_f32(word4, q4);
+      // Even lane: terms 0..7 from zero.  Odd lane: starts from the even
+      // lane's sums and adds terms 8..15, so each E keeps element order.
+      double s6 = 0.0, s4 = 0.0;
+      if (!odd) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const double a = (double)fabsf(w[j]);
+          const double d6 = __builtin_fma(-cs6, (double)fabsf(q6[j]), a);
+          const double d4 = __builtin_fma(-cs4, (double)fabsf(q4[j]), a);
+          s6 = s6 + d6 * d6;
+          s4 = s4 + d4 * d4;
+        }
+      }
+      s6 = __shfl_xor(s6, 1);
+      s4 = __shfl_xor(s4, 1);
+      if (odd) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const double a = (double)fabsf(w[j]);
+          const double d6 = __builtin_fma(-cs6, (double)fabsf(q6[j]), a);
+          const double d4 = __builtin_fma(-cs4, (double)fabsf(q4[j]), a);
+          s6 = s6 + d6 * d6;
+          s4 = s4 + d4 * d4;
+        }
+      }
+      const int pick4 = (odd && s4 < s6) ? 1 : 0;
+      const int use4 = __shfl(pick4, (int)(threadIdx.x | 1) & 63);  // the odd lane decides
+      if (use4) {
+        word = word4;
+        sc = k4;
+      }
+    }
+    __builtin_nontemporal_store(word, &codes[h]);
+    const uint32_t s1 = __shfl_down(sc, 2), s2 = __shfl_down(sc, 4), s3 = __shfl_down(sc, 6);
+    if (pack && (h | 7) < n_half) {
+      if ((h & 7) == 0) reinterpret_cast<uint32_t*>(scales)[h >> 3] = sc | (s1 << 8) | (s2 << 16) | (s3 << 24);
+    } else if ((h & 1) == 0) {
+      scales[h >> 1] = (uint8_t)sc;
+    }
+  }
+}
+
+hipError_t launch_quantize_4o6(const void* x, bool bf16, int64_t n_elems, const float* sg, uint8_t* codes,
+                               uint8_t* scales, hipStream_t stream) {
+  int64_t n_half = n_elems / 8;
+  if (n_half == 0) return hipSuccess;
+  int64_t wg = (n_half + 255) / 256;
+  if (wg > 8192) wg = 8192;
+  if (bf16)
+    hipLaunchKernelGGL(quantize_4o6_kernel<true>, dim3((unsigned)wg), dim3(256), 0, stream, x, n_half, sg,
+                       reinterpret_cast<uint32_t*>(codes), scales);
+  else
+    hipLaunchKernelGGL(quantize_4o6_kernel<false>, dim3((unsigned)wg), dim3(256), 0, stream, x, n_half, sg,
+                       reinterpret_cast<uint32_t*>(codes), scales);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize_absmax(const void* x, bool bf16, int64_t n_elems, const float* sg, uint8_t* codes,
                                   uint8_t* scales, hipStream_t stream) {
   int64_t n_half = n_elems / 8;

@@ -121,10 +121,7 @@ __device__ __forceinline__ double block_error_for_code(const float aw[16], const
   return err;
 }
 
-// kFourOverSix: the candidates are only the scales that map the block
-// maximum onto 6 (absmax) and onto 4 ("Tu pipeline NVFP4 ...", section 2,
-// algorithm table: four-over-six), same error and tie rule.
-template <bool kBF16, bool kFourOverSix>
+template <bool kBF16>
 __global__ __launch_bounds__(256) void quantize_mse_kernel(const void* __restrict__ x, int64_t nblocks,
                                                            const float* __restrict__ sg_ptr,
                                                            u32x2* __restrict__ codes, uint8_t* __restrict__ scales) {
@@ -145,22 +142,16 @@ __global__ __launch_bounds__(256) void quantize_mse_kernel(const void* __restric
     const double m = (double)mf;
     const double a = m / six_sg;
     const int kabs = (int)e4m3_code_rne(a);
-    int klo = 0, khi = 0, kfirst = kabs, ncand = 1, k4 = kabs;
-    if (kFourOverSix) {
-      k4 = (int)e4m3_code_rne(m / (4.0 * sg64));  // >= kabs
-      ncand = k4 != kabs ? 2 : 1;
-    } else {
-      // Window [k_lo, k_hi] of codes c >= 1 with a/2 <= c <= 2a (exact tests).
-      klo = (int)e4m3_code_rne(a * 0.5);
-      if (klo < 1) klo = 1;
-      if (12.0 * sg64 * (double)e4m3_to_f32(klo) < m) ++klo;
-      if (klo > 1 && 12.0 * sg64 * (double)e4m3_to_f32(klo - 1) >= m) --klo;
-      khi = (int)e4m3_code_rne(a * 2.0);
-      if (khi >= 1 && 3.0 * sg64 * (double)e4m3_to_f32(khi) > m) --khi;
-      if (khi < (int)kE4M3MaxCode && 3.0 * sg64 * (double)e4m3_to_f32(khi + 1) <= m) ++khi;
-      kfirst = min(klo, kabs);
-      ncand = max(khi, kabs) - kfirst + 1;
-    }
+    // Window [k_lo, k_hi] of codes c >= 1 with a/2 <= c <= 2a (exact tests).
+    int klo = (int)e4m3_code_rne(a * 0.5);
+    if (klo < 1) klo = 1;
+    if (12.0 * sg64 * (double)e4m3_to_f32(klo) < m) ++klo;
+    if (klo > 1 && 12.0 * sg64 * (double)e4m3_to_f32(klo - 1) >= m) --klo;
+    int khi = (int)e4m3_code_rne(a * 2.0);
+    if (khi >= 1 && 3.0 * sg64 * (double)e4m3_to_f32(khi) > m) --khi;
+    if (khi < (int)kE4M3MaxCode && 3.0 * sg64 * (double)e4m3_to_f32(khi + 1) <= m) ++khi;
+    const int kfirst = min(klo, kabs);
+    const int ncand = max(khi, kabs) - kfirst + 1;
 
     double aw64[16];
     uint32_t zoff[16];
@@ -173,8 +164,8 @@ __global__ __launch_bounds__(256) void quantize_mse_kernel(const void* __restric
     double best_err = 0.0;
     int best = -1;
     for (int i = 0; i < ncand; ++i) {
-      const int k = kFourOverSix ? (i == 0 ? kabs : k4) : kfirst + i;
-      if (!kFourOverSix && (k < klo || k > khi) && k != kabs) continue;
+      const int k = kfirst + i;
+      if ((k < klo || k > khi) && k != kabs) continue;
       const double err = block_error_for_code(aw, aw64, zoff, k, sg64, inv_sg);
       if (best < 0 || err < best_err) {
         best = k;
@@ -190,23 +181,17 @@ __global__ __launch_bounds__(256) void quantize_mse_kernel(const void* __restric
   }
 }
 
-hipError_t launch_quantize_search(const void* x, bool bf16, bool four_over_six, int64_t n_elems, const float* sg,
-                                  uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+hipError_t launch_quantize_mse(const void* x, bool bf16, int64_t n_elems, const float* sg, uint8_t* codes,
+                               uint8_t* scales, hipStream_t stream) {
   int64_t nb = n_elems / 16;
   if (nb == 0) return hipSuccess;
   int64_t wg = (nb + 255) / 256;
   if (wg > 16384) wg = 16384;
   u32x2* c = reinterpret_cast<u32x2*>(codes);
-#define NVFP4_QSEARCH(B, F) \
-  hipLaunchKernelGGL((quantize_mse_kernel<B, F>), dim3((unsigned)wg), dim3(256), 0, stream, x, nb, sg, c, scales)
-  if (bf16) {
-    if (four_over_six) NVFP4_QSEARCH(true, true);
-    else NVFP4_QSEARCH(true, false);
-  } else {
-    if (four_over_six) NVFP4_QSEARCH(false, true);
-    else NVFP4_QSEARCH(false, false);
-  }
-#undef NVFP4_QSEARCH
+  if (bf16)
+    hipLaunchKernelGGL(quantize_mse_kernel<true>, dim3((unsigned)wg), dim3(256), 0, stream, x, nb, sg, c, scales);
+  else
+    hipLaunchKernelGGL(quantize_mse_kernel<false>, dim3((unsigned)wg), dim3(256), 0, stream, x, nb, sg, c, scales);
   return hipGetLastError();
 }
 
