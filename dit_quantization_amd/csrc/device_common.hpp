@@ -170,6 +170,22 @@ __device__ __forceinline__ u32x4 smooth8(u32x4 v, f32x4 m0, f32x4 m1) {
   return o;
 }
 
+// s_waitcnt immediate for vmcnt(n) with lgkmcnt(0) (gfx9 encoding: vmcnt
+// in bits 3:0 and 15:14, expcnt left at its maximum 7).
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+
+// 16 (2) bytes per lane from a buffer straight into LDS: lane i of the wave
+// writes 16 bytes at lds_base + 16 i (the 2 bytes zero-extended to the dword
+// at lds_base + 4 i); offsets past the buffer write zeros.
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t buf, u32x4* lds_base, uint32_t voff,
+                                                uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(buf, (__attribute__((address_space(3))) void*)lds_base, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void buffer_to_lds2(__amdgpu_buffer_rsrc_t buf, uint32_t* lds_base, uint32_t voff,
+                                               uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(buf, (__attribute__((address_space(3))) void*)lds_base, 2, voff, soff, 0, 0);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

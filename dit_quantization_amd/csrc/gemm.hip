@@ -282,19 +282,6 @@ __device__ __forceinline__ f16x2 e4m3x2_to_f16x2(uint32_t b) {
 // s_waitcnt immediate: at most n vector memory operations outstanding, all
 // LDS operations complete (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt
 // 6:4 = 7 means no wait, lgkmcnt 11:8).
-constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
-
-// 16 (2) bytes per lane from a buffer straight into LDS: lane i of the wave
-// writes 16 bytes at lds_base + 16 i (the 2 bytes zero-extended to the dword
-// at lds_base + 4 i); offsets past the buffer write zeros.
-__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t buf, u32x4* lds_base, uint32_t voff,
-                                                uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(buf, (__attribute__((address_space(3))) void*)lds_base, 16, voff, soff, 0, 0);
-}
-__device__ __forceinline__ void buffer_to_lds2(__amdgpu_buffer_rsrc_t buf, uint32_t* lds_base, uint32_t voff,
-                                               uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(buf, (__attribute__((address_space(3))) void*)lds_base, 2, voff, soff, 0, 0);
-}
 
 // BM x BN tile per workgroup of WM x WN waves; each wave (BM/WM) x (BN/WN)
 // as TM x TN tiles of 32x32.  grid.x enumerates tiles (XCD-aware order).

@@ -7,10 +7,13 @@
 // M > 1 design (gfx950): a workgroup of NW waves owns 16 * T weight rows;
 // its waves split K.  K is read in super-chunks of 128 (4 chunks of 32
 // codes = 16 bytes per row), 4 super-chunks per pass.  Lane (n, g) of a wave
-// (n = lane % 16, g = lane / 16) loads chunk 4s + g of row n, so one load
-// instruction reads 16 rows x 64 contiguous bytes, and unpacks its 4 code
-// dwords to exact bf16 values q * s_b (<= 6 significant bits, magnitudes in
-// [2^-10, 2688]) as the B operands of 4 v_mfma_f32_16x16x32_bf16.  The
+// (n = lane % 16, g = lane / 16) takes chunk 4s + g of row n and unpacks its
+// 4 code dwords to exact bf16 values q * s_b (<= 6 significant bits,
+// magnitudes in [2^-10, 2688]) as the B operands of 4
+// v_mfma_f32_16x16x32_bf16.  The codes of a pass reach LDS by DMA with every
+// instruction reading 4 rows x 256 contiguous bytes (measured 1.3-2.7 us per
+// 33 MB call faster than loading 16 rows x 64 bytes straight into the MFMA
+// layout), and each lane reads its chunks back from a row-swizzled slot.  The
 // scales of a pass come from one 8-byte load per lane, redistributed between
 // the 4 lanes of a row with two cross-lane exchanges.  The vector memory
 // pipe bounds this kernel, so the x operand is built from as few load
@@ -90,7 +93,9 @@ __global__ __launch_bounds__(NW * 64) void gemv_w4a16_kernel(const uint16_t* __r
                                                              float* __restrict__ partial) {
   constexpr int SW = 4;              // super-chunks per pass (one 8-byte scale load per lane)
   constexpr int XL = DENSE ? 4 : 1;  // x loads per super-chunk
-  __shared__ f32x4 red[NW][T][64];
+  // Per wave and row tile: the pass's 16 rows x 16 code chunks, staged
+  // global -> LDS; the reduction at the end reuses the wave's own region.
+  __shared__ u32x4 lds_c[NW][T][256];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nl = lane & 15, g = lane >> 4;
@@ -151,15 +156,29 @@ __global__ __launch_bounds__(NW * 64) void gemv_w4a16_kernel(const uint16_t* __r
         }
       }
     }
+    // Codes: DMA instruction u of tile t fills LDS slots [64 u, 64 u + 64):
+    // lane l -> row r = 4 u + l / 16, slot j = l % 16, holding chunk
+    // 4 s0 + (j ^ r), so each instruction reads 4 rows x 256 contiguous bytes
+    // (a permutation of the pass's 16 chunks per row).  Chunks of
+    // super-chunks past this wave's range, or past K, read as zero.
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int u = 0; u < SW; ++u) {
+        const int r = 4 * u + (lane >> 4);
+        const int c = 4 * s0 + ((lane & 15) ^ r);
+        const bool ok = c < 4 * send && c < nch;
+        buffer_to_lds16(cbuf, &lds_c[wave][t][64 * u], ok ? (16 * t + r) * half + 16 * c : kBufOOB, 0);
+      }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    // Lane (n, g) reads chunk 4 (s0 + u) + g of row n from slot (4 u + g) ^ n:
+    // the 16 lanes of a group hit 16 different slots of 16 rows (no bank
+    // conflicts).
     u32x4 cw[SW][T];
 #pragma unroll
-    for (int u = 0; u < SW; ++u) {
-      const int c = 4 * (s0 + u) + g;
-      const bool ok = s0 + u < send && c < nch;
+    for (int u = 0; u < SW; ++u)
 #pragma unroll
-      for (int t = 0; t < T; ++t)
-        cw[u][t] = __builtin_amdgcn_raw_buffer_load_b128(cbuf, ok ? (16 * t + nl) * half + 16 * c : kBufOOB, 0, kBufNT);
-    }
+      for (int t = 0; t < T; ++t) cw[u][t] = lds_c[wave][t][16 * nl + ((4 * u + g) ^ nl)];
     __builtin_amdgcn_sched_barrier(0);
     uint32_t pairs[T][4];
 #pragma unroll
@@ -186,22 +205,24 @@ __global__ __launch_bounds__(NW * 64) void gemv_w4a16_kernel(const uint16_t* __r
   // dense: lane (n, g) holds rows m = 4 g + i.  staggered: lane (n, g) holds
   // rows 4 g + i = x row i times the codes of MFMA g; the sum over the lane
   // groups leaves row m = g in lane (n, g).
+  // (each wave's partial sums go to the first T KB of its own code region)
+  f32x4* const red_w = reinterpret_cast<f32x4*>(&lds_c[wave][0][0]);
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     if (DENSE) {
-      red[wave][t][lane] = acc[t];
+      red_w[64 * t + lane] = acc[t];
     } else {
       const float v = group_sum4(acc[t], lane);
-      red[wave][t][lane] = f32x4{v, 0.f, 0.f, 0.f};
+      red_w[64 * t + lane] = f32x4{v, 0.f, 0.f, 0.f};
     }
   }
   __syncthreads();
   const float sg = *sg_ptr;
   for (int idx = threadIdx.x; idx < T * 64; idx += NW * 64) {
     const int t = idx >> 6, l = idx & 63;
-    f32x4 sum = red[0][t][l];
+    f32x4 sum = reinterpret_cast<const f32x4*>(&lds_c[0][0][0])[64 * t + l];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) sum += red[w][t][l];
+    for (int w = 1; w < NW; ++w) sum += reinterpret_cast<const f32x4*>(&lds_c[w][0][0])[64 * t + l];
     const int n = n0 + 16 * t + (l & 15);
 #pragma unroll
     for (int i = 0; i < (DENSE ? 4 : 1); ++i) {
@@ -410,10 +431,11 @@ hipError_t launch_gemv_w4a16(const uint16_t* x, const uint8_t* codes, const uint
     return hipGetLastError();
   }
   // M > 1: MFMA kernels.  On weights of at least 8192 rows, 32 rows per
-  // workgroup (M <= 4) or 64 (M > 4: each x fragment then feeds 4 row tiles,
-  // and x is read from L2 once per workgroup; 14336 x 4096 at M = 16: 15.0 us
-  // against 17.1 us with 32 rows); else 16 rows, with 16 waves splitting
-  // rows of K >= 8192 (unless the split-K path above took the call).
+  // workgroup of 4 waves (M <= 4) or 64 rows of 8 waves (M > 4: each x
+  // fragment then feeds 4 row tiles, and x is read from L2 once per
+  // workgroup); else 16 rows, with 16 waves splitting rows of K >= 8192
+  // (unless the split-K path above took the call).  Chosen by sweeping rows
+  // x waves on the 14336 x 4096 and 4096 x 14336 decode shapes.
   const int dense = M > 4 ? 1 : 0;
   const bool t2 = N >= 32 * 256;
   const bool nw16 = !t2 && K >= 8192;
@@ -435,7 +457,7 @@ hipError_t launch_gemv_w4a16(const uint16_t* x, const uint8_t* codes, const uint
     else if (nw16) NVFP4_GEMV_MFMA(1, 1, 16);
     else NVFP4_GEMV_MFMA(1, 1, 8);
   } else {
-    if (t2) NVFP4_GEMV_MFMA(0, 2, 8);
+    if (t2) NVFP4_GEMV_MFMA(0, 2, 4);
     else if (nw16) NVFP4_GEMV_MFMA(0, 1, 16);
     else NVFP4_GEMV_MFMA(0, 1, 8);
   }
