@@ -116,8 +116,8 @@ def mse_candidates(x, sg):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU split of this path is "
-              "described in DESIGN.md and not built", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this library has no multi-GPU path "
+              "(the products would shard column-parallel over weight rows, one process per GPU)", file=sys.stderr)
         sys.exit(2)
     import torch
     from dit_quantization_amd import inputs

@@ -23,7 +23,7 @@
  *        packed uint8 [out, in/2] codes, float8_e4m3fn [out, in/16] scales,
  *        out = (A*s_a)(B*s_b)^T with a 16-bit output, activations quantized on
  *        every call.
- * Readings where the pages are silent (each also listed in the design doc):
+ * Readings where the pages are silent (fixed identically on the GPU side):
  *   R1 nibble order: low nibble = even column.          R2 canonical +0 code.
  *   R3 s_g = fp32(amax_T / (6*448)); amax_T == 0 -> 1.  R4 ties to the even code
  *   (E2M1 and E4M3), E4M3 saturates at 448.              R5 MSE candidates: the
