@@ -240,14 +240,19 @@ __global__ __launch_bounds__(NW * 64) void gemv_w4a16_kernel(const uint16_t* __r
 }
 
 // ---- M = 1: VALU dot products.
-// A workgroup (4 waves) owns RW rows; its waves split K into S parts and the
-// 4/S row groups split the rows.  Lane l of a wave owns the 16-byte code
-// chunks l, l + 64, ... of its K part (chunk c = codes of k in [32c, 32c+32)),
-// so one load instruction reads 1 KB of a row contiguously, and the lane
-// keeps x for its k's in registers for all of its rows.  Codes become bf16
-// pairs with the hardware converter (scale-free q values, exact);
+// A workgroup (4 waves) owns RW rows per row group; its waves split K into S
+// parts and the 4/S row groups split the rows.  Lane l of a wave owns the
+// 16-byte code chunks l, l + 64, ... of its K part (chunk c = codes of k in
+// [32c, 32c+32)), so one load instruction reads 1 KB of a row contiguously,
+// and the lane keeps x for its k's in registers for all of its rows.  Codes
+// become bf16 pairs with the hardware converter (scale-free q values, exact);
 // v_dot2_f32_bf16 multiplies them with x pairs; each 16-element block sum is
-// multiplied by its scale.  Rows are reduced across the wave with a
+// multiplied by its scale, decoded by the hardware FP8 (E4M3) converter.
+// Every load is a buffer load; lanes past the K part (or rows past N) read
+// zeros, so their contribution is exactly 0 with no per-lane select.  The
+// loads are issued row by row and the rows are computed in the same order
+// (scheduling barriers), so a wave starts on its first row while the later
+// rows' loads are still in flight.  Rows are reduced across the wave with a
 // transposing butterfly, then across the S waves in LDS.
 __device__ __forceinline__ void fp4x8_to_bf16x2(uint32_t c, uint32_t v[4]) {
   v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 0));
@@ -308,46 +313,47 @@ __global__ __launch_bounds__(256) void gemv_m1_kernel(const uint16_t* __restrict
                                                       void* __restrict__ out) {
   constexpr int G = 4 / S;                 // row groups per workgroup
   __shared__ float red[4][RW];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int part = wave % S, grp = wave / S;
   const int nch = K / 32;
   const int per = (nch + S - 1) / S;       // chunks in each K part
   const int cbeg = part * per, cend = min(cbeg + per, nch);
   const int row0 = (blockIdx.x * G + grp) * RW;
-  // x for this lane's chunks (16 dwords = 32 bf16 per chunk), clamped past the part
+  // this wave's rows (none past N: a row group past the end reads only zeros)
+  const int nrows = __builtin_amdgcn_readfirstlane(max(0, min(RW, N - row0)));
+  const int64_t rb = min(row0, N - 1);
+  const __amdgpu_buffer_rsrc_t cbuf = make_buf(codes + rb * (K / 2), (uint32_t)(nrows * (K / 2)));
+  const __amdgpu_buffer_rsrc_t sbuf = make_buf(scales + rb * (K / 16), (uint32_t)(nrows * (K / 16)));
+  const __amdgpu_buffer_rsrc_t xbuf = make_buf(x, (uint32_t)(K * 2));
+  // x for this lane's chunks (16 dwords = 32 bf16 per chunk)
   uint32_t xr[CH][16];
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    const int ch = min(cbeg + lane + 64 * c, nch - 1);
+    const int ch = cbeg + lane + 64 * c;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(x + 32 * ch + 8 * q);
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xbuf, ch < cend ? 64 * ch + 16 * q : kBufOOB, 0, 0);
       xr[c][4 * q] = v.x; xr[c][4 * q + 1] = v.y; xr[c][4 * q + 2] = v.z; xr[c][4 * q + 3] = v.w;
     }
   }
-  // all weight loads of this wave first
   u32x4 cw[RW][CH];
   uint32_t sw[RW][CH];
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
-    const int row = min(row0 + r, N - 1);
-    const uint8_t* crow = codes + (int64_t)row * (K / 2);
-    const uint8_t* srow = scales + (int64_t)row * (K / 16);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int ch = min(cbeg + lane + 64 * c, nch - 1);
-      cw[r][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(crow + 16 * ch));
-      sw[r][c] = *reinterpret_cast<const uint16_t*>(srow + 2 * ch);
+      const int ch = cbeg + lane + 64 * c;
+      cw[r][c] = __builtin_amdgcn_raw_buffer_load_b128(cbuf, ch < cend ? r * (K / 2) + 16 * ch : kBufOOB, 0, kBufNT);
+      sw[r][c] = __builtin_amdgcn_raw_buffer_load_b16(sbuf, ch < cend ? r * (K / 16) + 2 * ch : kBufOOB, 0, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);     // issue order = row order
   }
-  __builtin_amdgcn_sched_barrier(0);
   float acc[RW];
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     acc[r] = 0.0f;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const bool live = cbeg + lane + 64 * c < cend;
       uint32_t q[16];
       fp4x8_to_bf16x2(cw[r][c].x, q);
       fp4x8_to_bf16x2(cw[r][c].y, q + 4);
@@ -358,9 +364,10 @@ __global__ __launch_bounds__(256) void gemv_m1_kernel(const uint16_t* __restrict
       for (int i = 0; i < 8; ++i) p0 = dot2(xr[c][i], q[i], p0);
 #pragma unroll
       for (int i = 8; i < 16; ++i) p1 = dot2(xr[c][i], q[i], p1);
-      const float s0 = e4m3_to_f32(sw[r][c] & 0xFFu), s1 = e4m3_to_f32(sw[r][c] >> 8);
-      acc[r] = live ? __builtin_fmaf(p1, s1, __builtin_fmaf(p0, s0, acc[r])) : acc[r];
+      const f32x2 s = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw[r][c], 1.0f, false);  // bytes 0, 1 (exact)
+      acc[r] = __builtin_fmaf(p1, s[1], __builtin_fmaf(p0, s[0], acc[r]));
     }
+    __builtin_amdgcn_sched_barrier(0);     // compute order = row order
   }
   const float tot = wave_sum_rows<RW>(acc, lane);
   if ((lane & (64 / RW - 1)) == 0) red[wave][reduced_row<RW>(lane)] = tot;
@@ -424,8 +431,11 @@ hipError_t launch_gemv_w4a16(const uint16_t* x, const uint8_t* codes, const uint
 #define NVFP4_GEMV_M1(CH, RW, S)                                                                                  \
   hipLaunchKernelGGL((gemv_m1_kernel<CH, RW, S>), dim3((unsigned)((N + (4 / S) * RW - 1) / ((4 / S) * RW))),      \
                      dim3(256), 0, stream, x, codes, scales, sg, (int)N, (int)K, b, y)
-    if (nch <= 2 * 64) NVFP4_GEMV_M1(1, 8, 2);          // K <= 4096: halves of the row per wave
-    else if (nch <= 4 * 128) NVFP4_GEMV_M1(2, 8, 4);    // K <= 16384: quarters
+    // 4 rows per wave (8 rows per wave leaves each wave's arithmetic after
+    // most of its loads have landed); K in 2 parts up to 16384, else 4.
+    if (nch <= 2 * 64) NVFP4_GEMV_M1(1, 4, 2);          // K <= 4096
+    else if (nch <= 2 * 128) NVFP4_GEMV_M1(2, 4, 2);    // K <= 8192
+    else if (nch <= 2 * 256) NVFP4_GEMV_M1(4, 4, 2);    // K <= 16384
     else NVFP4_GEMV_M1(4, 4, 4);                         // K <= 32768
 #undef NVFP4_GEMV_M1
     return hipGetLastError();

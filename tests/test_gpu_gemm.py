@@ -61,6 +61,24 @@ def test_gemv_ragged(shape, M):
     assert_bracket_bf16(yb.reshape(-1), ystar, tau, "bf16")
 
 
+@pytest.mark.parametrize("shape", [(37, 6144), (20, 12320), (9, 32768), (70, 16384)])
+def test_gemv_m1_long_rows(shape):
+    """M = 1 with every row-length class of the single-row kernel: K <= 8192
+    (2 chunks a lane), <= 16384 (4 chunks, 2 K parts; 12320 leaves K parts
+    with idle lanes) and <= 32768 (4 K parts); N not a multiple of the 8 rows
+    a workgroup covers."""
+    N, K = shape
+    print(f"[case] gemv M=1 N={N} K={K}", flush=True)
+    w = inputs.student_t_f32((N, K), N + 3 * K)
+    xb = inputs.gemv_x(K, 1)
+    c, s, g = _quant_weight(w, oracle.MSE)
+    oc, os_, og = _oracle_weight(c)
+    ystar, tau = oracle.dot_w4a16(inputs.bf16_bits_to_f32(xb), oc, os_, og)
+    y32 = host(nv.gemv_w4a16(dev_bf16(xb), c, s, g, out_dtype=torch.float32))
+    assert_within_tau(y32.reshape(-1), ystar, tau, "fp32")
+    assert_bracket_bf16(host(nv.gemv_w4a16(dev_bf16(xb), c, s, g)).reshape(-1), ystar, tau, "bf16")
+
+
 @pytest.mark.parametrize("shape", [(300, 8320), (1000, 16384), (64, 8192)])
 @pytest.mark.parametrize("M", [5, 16])
 def test_gemv_splitk(shape, M):
