@@ -79,6 +79,17 @@ __device__ __forceinline__ void scale_pairs(u32x2 d, int lane, uint32_t pair[4])
   }
 }
 
+// s_waitcnt until at most k groups of G vector memory instructions newer
+// than the awaited one are outstanding (k < 4; the count must be an
+// immediate).
+template <int G>
+__device__ __forceinline__ void wait_vm_newer(int k) {
+  if (k == 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+  else if (k == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(G));
+  else if (k == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * G));
+  else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(3 * G));
+}
+
 // grid: ceil(N / (16 T)) workgroups of NW waves (times `splits` with
 // SPLIT).  DENSE: the M > 4 operand layout; otherwise staggered (M <= 4).
 // SPLIT: workgroup b takes super-chunk range b % splits of row block
@@ -170,35 +181,57 @@ __global__ __launch_bounds__(NW * 64) void gemv_w4a16_kernel(const uint16_t* __r
         const bool ok = c < 4 * send && c < nch;
         buffer_to_lds16(cbuf, &lds_c[wave][t][64 * u], ok ? (16 * t + r) * half + 16 * c : kBufOOB, 0);
       }
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    uint32_t pairs[T][4];
     // Lane (n, g) reads chunk 4 (s0 + u) + g of row n from slot (4 u + g) ^ n:
     // the 16 lanes of a group hit 16 different slots of 16 rows (no bank
     // conflicts).
-    u32x4 cw[SW][T];
+    auto mfma4 = [&](int u, int t, const u32x4& cw) {
+      const f32x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(pairs[t][u], 1.0f, false);
 #pragma unroll
-    for (int u = 0; u < SW; ++u)
-#pragma unroll
-      for (int t = 0; t < T; ++t) cw[u][t] = lds_c[wave][t][16 * nl + ((4 * u + g) ^ nl)];
-    __builtin_amdgcn_sched_barrier(0);
-    uint32_t pairs[T][4];
-#pragma unroll
-    for (int t = 0; t < T; ++t) scale_pairs(sw[t], lane, pairs[t]);
-#pragma unroll
-    for (int u = 0; u < SW; ++u) {
-      if (s0 + u < send) {  // wave-uniform
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-          const f32x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(pairs[t][u], 1.0f, false);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const u32x4 z4 = {0u, 0u, 0u, 0u};
-            const u32x4 a = DENSE ? xa[u][DENSE ? j : 0] : (jx == j ? xa[u][0] : z4);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                             fp4x8_to_bf16x8_scaled(cw[u][t][j], j < 2 ? sc.x : sc.y),
-                                                             acc[t], 0, 0, 0);
-          }
-        }
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 z4 = {0u, 0u, 0u, 0u};
+        const u32x4 a = DENSE ? xa[u][DENSE ? j : 0] : (jx == j ? xa[u][0] : z4);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                         fp4x8_to_bf16x8_scaled(cw[j], j < 2 ? sc.x : sc.y),
+                                                         acc[t], 0, 0, 0);
       }
+    };
+    if constexpr (DENSE) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) scale_pairs(sw[t], lane, pairs[t]);
+      // Tile by tile: tile t's rows come only from its own SW instructions,
+      // issued in tile order, so tile t is complete once SW (T - 1 - t)
+      // newer loads are outstanding (loads, LDS DMA included, complete in
+      // issue order) and its MFMAs overlap the later tiles' DMA.
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm_newer<SW>(T - 1 - t);
+        __builtin_amdgcn_sched_barrier(0);
+        u32x4 cw[SW];
+#pragma unroll
+        for (int u = 0; u < SW; ++u) cw[u] = lds_c[wave][t][16 * nl + ((4 * u + g) ^ nl)];
+#pragma unroll
+        for (int u = 0; u < SW; ++u)
+          if (s0 + u < send) mfma4(u, t, cw[u]);  // wave-uniform
+      }
+    } else {
+      // Staggered (2-tile workgroups): one wait for the pass, and the tiles'
+      // independent accumulators interleaved (faster here: measured).
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+      u32x4 cw[SW][T];
+#pragma unroll
+      for (int u = 0; u < SW; ++u)
+#pragma unroll
+        for (int t = 0; t < T; ++t) cw[u][t] = lds_c[wave][t][16 * nl + ((4 * u + g) ^ nl)];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < T; ++t) scale_pairs(sw[t], lane, pairs[t]);
+#pragma unroll
+      for (int u = 0; u < SW; ++u)
+        if (s0 + u < send)  // wave-uniform
+#pragma unroll
+          for (int t = 0; t < T; ++t) mfma4(u, t, cw[u][t]);
     }
   }
 
