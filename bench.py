@@ -254,6 +254,21 @@ def main():
         capture("gemm_prefill_up_reuse", prefill_up, flops=2.0 * M * N * K,
                 nbytes=M * K * 2 + N * K * 0.5625 + 2 * M * N)
 
+    # The image and text streams of a double-stream DiT block are independent
+    # until the joint attention: their products run on two HIP streams (both
+    # at the default priority), forked from and joined back into the timed
+    # stream, so the short text-stream products fill CUs that the image
+    # stream's leave idle.
+    side = torch.cuda.Stream()
+
+    def two_streams(run_img, run_txt):
+        main = torch.cuda.current_stream()
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            run_txt()
+        run_img()
+        main.wait_stream(side)
+
     if "gemm" in phases or "dit" in phases:
         log("[setup] dit block")
         a_img, a_txt, h_img, h_txt = inputs.dit_activations()
@@ -274,13 +289,15 @@ def main():
             for name, (c, s, g) in w.items():
                 dit_flops += 2.0 * ad.shape[0] * c.shape[0] * c.shape[1] * 2
 
+        def dit_stream(ad, hd, w, ws_a, ws_h, outs):
+            nv.gemm_w4a4(ad, *w["to_q"], workspace=ws_a, out=outs["to_q"])
+            nv.gemm_w4a4(ad, *w["to_k"], workspace=ws_a, out=outs["to_k"], reuse_act=True)
+            nv.gemm_w4a4(ad, *w["to_v"], workspace=ws_a, out=outs["to_v"], reuse_act=True)
+            nv.gemm_w4a4(ad, *w["mlp_up"], workspace=ws_a, out=outs["mlp_up"])   # the MLP input is quantized anew
+            nv.gemm_w4a4(hd, *w["mlp_down"], workspace=ws_h, out=outs["mlp_down"])
+
         def dit_block():
-            for ad, hd, w, ws_a, ws_h, outs in dit_calls:
-                nv.gemm_w4a4(ad, *w["to_q"], workspace=ws_a, out=outs["to_q"])
-                nv.gemm_w4a4(ad, *w["to_k"], workspace=ws_a, out=outs["to_k"], reuse_act=True)
-                nv.gemm_w4a4(ad, *w["to_v"], workspace=ws_a, out=outs["to_v"], reuse_act=True)
-                nv.gemm_w4a4(ad, *w["mlp_up"], workspace=ws_a, out=outs["mlp_up"])   # the MLP input is quantized anew
-                nv.gemm_w4a4(hd, *w["mlp_down"], workspace=ws_h, out=outs["mlp_down"])
+            two_streams(lambda: dit_stream(*dit_calls[0]), lambda: dit_stream(*dit_calls[1]))
 
         capture("gemm_dit_block", dit_block, flops=dit_flops)
 
@@ -359,13 +376,17 @@ def main():
                 lora_flops += 2.0 * Ms * N * K + 2.0 * Ms * 32 * (K + N)
             del layers
 
+        n_img = len(lora_calls) // 2   # the image stream's layers come first
+
+        def lora_layers(calls, svdq):
+            for act, wq, down, up, wsl, out, smooth in calls:
+                nv.gemm_w4a4(act, *wq, workspace=wsl, out=out, lora=(down, up), smooth=smooth if svdq else None)
+
         def dit_block_lora():
-            for act, wq, down, up, wsl, out, _ in lora_calls:
-                nv.gemm_w4a4(act, *wq, workspace=wsl, out=out, lora=(down, up))
+            two_streams(lambda: lora_layers(lora_calls[:n_img], False), lambda: lora_layers(lora_calls[n_img:], False))
 
         def dit_block_svdq():
-            for act, wq, down, up, wsl, out, smooth in lora_calls:
-                nv.gemm_w4a4(act, *wq, workspace=wsl, out=out, lora=(down, up), smooth=smooth)
+            two_streams(lambda: lora_layers(lora_calls[:n_img], True), lambda: lora_layers(lora_calls[n_img:], True))
 
         capture("lora_dit_block", dit_block_lora, flops=lora_flops)
         capture("svdq_dit_block", dit_block_svdq, flops=lora_flops)
