@@ -42,7 +42,7 @@ import numpy as np
 HBM_PEAK = 8.0e12           # bytes/s
 MFMA16_PEAK = 2.5e15        # dense fp16/bf16 MFMA flop/s
 VALU_PEAK = 256 * 64 * 2.4e9  # non-packed fp32/fp64 lane-ops/s: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz
-GEMV_COPIES = 8             # 8 x 33 MB > 256 MB MALL
+GEMV_COPIES = 16            # 16 x 33 MB = 529 MB, twice the 256 MB MALL (8 copies measured the same)
 
 
 def parse():
