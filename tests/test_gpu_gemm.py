@@ -247,6 +247,24 @@ def test_gemm_and_gemv_deterministic():
     assert np.array_equal(v1, v2)
 
 
+@pytest.mark.parametrize("which", [0, 1])
+def test_gemv_deterministic_decode_shapes(which):
+    """Every GEMV kernel repeats bit for bit at full size (M = 1, 4, 16 on both
+    decode shapes, fp32 out, ten calls each; rotating two weight copies so
+    the calls read from HBM)."""
+    w = inputs.gemv_weights()[which]
+    N, K = w.shape
+    c, s, g = _quant_weight(w)
+    copies = [(c, s), (c.clone(), s.clone())]
+    xb = dev_bf16(inputs.gemv_x(K, 16))
+    for M in (1, 4, 16):
+        print(f"[case] gemv repeat N={N} K={K} M={M}", flush=True)
+        outs = [host(nv.gemv_w4a16(xb[:M].contiguous(), cc, ss, g, out_dtype=torch.float32))
+                for i in range(10) for cc, ss in [copies[i % 2]]]
+        for o in outs[1:]:
+            assert np.array_equal(o, outs[0])
+
+
 @pytest.mark.parametrize("M", [1, 5])
 def test_gemv_maximum_k(M):
     """K = 2^24, the largest the decode product accepts (N = 16 rows; M = 5 also
