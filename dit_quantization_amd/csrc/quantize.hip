@@ -270,17 +270,25 @@ __global__ __launch_bounds__(256) void quantize_4o6_kernel(const void* __restric
       float q6[8], q4[8];
       fp4x8_to_f32(word6, q6);
       fp4x8_to_f32(word4, q4);
-      // Even lane: terms 0..7 from zero.  Odd lane: starts from the even
-      // lane's sums and adds terms 8..15, so each E keeps element order.
+      // Every lane squares its 8 errors per candidate (d = |w| - c s_g |q|,
+      // one rounding: the product is exact).  Only the sums are ordered: the
+      // even lane adds terms 0..7 from zero, the odd lane continues from the
+      // even lane's sums with terms 8..15, so each E keeps element order.
+      double sq6[8], sq4[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const double a = (double)fabsf(w[j]);
+        const double d6 = __builtin_fma(-cs6, (double)fabsf(q6[j]), a);
+        const double d4 = __builtin_fma(-cs4, (double)fabsf(q4[j]), a);
+        sq6[j] = d6 * d6;
+        sq4[j] = d4 * d4;
+      }
       double s6 = 0.0, s4 = 0.0;
       if (!odd) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const double a = (double)fabsf(w[j]);
-          const double d6 = __builtin_fma(-cs6, (double)fabsf(q6[j]), a);
-          const double d4 = __builtin_fma(-cs4, (double)fabsf(q4[j]), a);
-          s6 = s6 + d6 * d6;
-          s4 = s4 + d4 * d4;
+          s6 = s6 + sq6[j];
+          s4 = s4 + sq4[j];
         }
       }
       s6 = __shfl_xor(s6, 1);
@@ -288,11 +296,8 @@ __global__ __launch_bounds__(256) void quantize_4o6_kernel(const void* __restric
       if (odd) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const double a = (double)fabsf(w[j]);
-          const double d6 = __builtin_fma(-cs6, (double)fabsf(q6[j]), a);
-          const double d4 = __builtin_fma(-cs4, (double)fabsf(q4[j]), a);
-          s6 = s6 + d6 * d6;
-          s4 = s4 + d4 * d4;
+          s6 = s6 + sq6[j];
+          s4 = s4 + sq4[j];
         }
       }
       const int pick4 = (odd && s4 < s6) ? 1 : 0;
