@@ -259,8 +259,10 @@ __global__ __launch_bounds__(256) void quantize_4o6_kernel(const void* __restric
 #pragma unroll
     for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(w[j]));
     m = fmaxf(m, __shfl_xor(m, 1));
-    const uint32_t k6 = e4m3_code_rne((double)m / (6.0 * sg64));
-    const uint32_t k4 = e4m3_code_rne((double)m / (4.0 * sg64));  // >= k6
+    // the even lane rounds max|W| / (6 s_g), the odd lane max|W| / (4 s_g); they swap
+    const uint32_t kk = e4m3_code_rne((double)m / ((odd ? 4.0 : 6.0) * sg64));
+    const uint32_t ko = (uint32_t)__shfl_xor((int)kk, 1);
+    const uint32_t k6 = odd ? ko : kk, k4 = odd ? kk : ko;  // k4 >= k6
     const float c6 = e4m3_to_f32(k6), c4 = e4m3_to_f32(k4);
     const uint32_t word6 = encode8(w, c6, sg, inv_sg);
     uint32_t word = word6, sc = k6;
