@@ -503,14 +503,21 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu((B
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     dma(cur, kt + 3);
-    __builtin_amdgcn_sched_barrier(0);
+    // With at least as many MFMAs in the last sub-step as DMA instructions
+    // (256 x 256 tiles), the DMA is interleaved with them (one per MFMA:
+    // prefill 367 -> 358 us on constant operands); otherwise it goes out as
+    // one burst before them (faster for 128 x 128 tiles).
+    constexpr bool kInterleaveDma = TM * TN >= VM_STEP;
+    if (!kInterleaveDma) __builtin_amdgcn_sched_barrier(0);
     // sub-step 3 uses buffer 1; the next stage's first operands go to buffer 0
     substep(cur, 3);
     load_first(nxt);
     // reads first (one per MFMA), the unpack in the second half
     constexpr int kReads = TM + 2 * TN, kMF = TM * TN;
+    constexpr int kVmem = 0x020;
 #pragma unroll
     for (int q = 0; q < kMF; ++q) {
+      if (kInterleaveDma && q < VM_STEP) __builtin_amdgcn_sched_group_barrier(kVmem, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kMFMA, 1, 0);
       if (q < kReads) __builtin_amdgcn_sched_group_barrier(kDSR, 1, 0);
       if (q >= kMF / 2) __builtin_amdgcn_sched_group_barrier(kVALU, (8 * TN + 6 + kMF / 2 - 1) / (kMF / 2), 0);
