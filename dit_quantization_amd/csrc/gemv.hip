@@ -15,9 +15,10 @@
 // 33 MB call faster than loading 16 rows x 64 bytes straight into the MFMA
 // layout), and each lane reads its chunks back from a row-swizzled slot.  The
 // scales of a pass come from one 8-byte load per lane, redistributed between
-// the 4 lanes of a row with two cross-lane exchanges.  The vector memory
-// pipe bounds this kernel, so the x operand is built from as few load
-// instructions as possible:
+// the 4 lanes of a row with two cross-lane exchanges.  The loads alone take
+// about two thirds of a call; the decode with its per-element block-scale
+// multiply and, at M > 4, the x loads take the rest, so the x operand is
+// built from as few load instructions as possible:
 //  * M <= 4 (staggered): lane (4 j + i, g) loads the 8 values of x[i] that
 //    meet MFMA j in lane group g -- one 16-byte load per lane covers all 4
 //    MFMAs of a super-chunk.  MFMA j keeps only the lanes with j' == j, so
@@ -26,9 +27,10 @@
 //  * M > 4 (dense): lane (m, g) holds x[m] on its lane group's k slots for
 //    each MFMA; 4 loads per super-chunk cover 16 rows.
 // Rows past N, chunks past K and x rows past M are buffer loads at an
-// out-of-range offset, which return zero without a memory access.  Waves
-// are added in LDS in wave order; the epilogue multiplies by s_g and rounds
-// to bf16 (RNE).  Workgroups of 16 (or 32 / 64 rows on tall weights) read x
+// out-of-range offset, which return zero without a memory access.  With the
+// dense layout each 16-row tile is computed as soon as its own DMA has
+// landed.  Waves are added in LDS in wave order; the epilogue multiplies by
+// s_g and rounds to bf16 (RNE).  Workgroups of 16 (or 32 / 64 rows on tall weights) read x
 // from L2 once each; M > 4 on short weights with long rows splits K over
 // workgroups instead (partial sums added in range order by a second pass).
 #include "device_common.hpp"
