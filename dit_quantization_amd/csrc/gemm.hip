@@ -11,14 +11,15 @@
 //    quantizer), written out as the exact fp16 values q_a * s_a (<= 6
 //    significant bits, magnitudes in [2^-10, 2688], so fp16 holds them
 //    exactly and the bf16/fp16 matrix cores can consume them directly).
-//  * gemm: 256x256 (or 128x128) output tiles per workgroup of 4 waves in a
-//    2x2 arrangement, K step 64.  A^ tiles go global -> registers -> LDS
-//    (XOR-swizzled 16-byte chunks, double buffered).  Packed weights go
-//    global -> registers; each lane unpacks its 32 codes with the hardware
-//    FP4 converter and one packed fp16 multiply by the block scale, giving
-//    exact fp16 q_w * s_w operands.  v_mfma_f32_32x32x16_f16 accumulates in
-//    fp32 (every product is exact); the epilogue multiplies by
-//    fp32(s_gA * s_gW) and rounds to bf16.
+//  * gemm: 256x256 output tiles per workgroup of 8 waves (128x64 each), or
+//    128x128 tiles of 4 waves for short activations, K step 64.  A^ tiles,
+//    packed weight codes and their scales go global -> LDS directly (buffer
+//    loads with the LDS bit) into three stages fetched ahead; A^ chunks sit
+//    XOR-swizzled so 16-byte fragment reads are conflict-free.  Each lane
+//    unpacks its weight codes with the hardware FP4 converter and one packed
+//    fp16 multiply by the block scale, giving exact fp16 q_w * s_w operands.
+//    v_mfma_f32_32x32x16_f16 accumulates in fp32 (every product is exact);
+//    the epilogue multiplies by fp32(s_gA * s_gW) and rounds to bf16.
 //  * The k order inside each 64-wide K step is permuted identically for A
 //    and W (lane group g of an MFMA feeds k = 32 g + 8 s + j at sub-step s),
 //    which lets every lane read 16 contiguous bytes of packed weights.
@@ -148,7 +149,8 @@ __global__ __launch_bounds__(256) void act_quant_lora_kernel(const uint16_t* __r
     for (int u = 0; u < U; ++u) {
       const int c = c0 + 4 * u;
       const int k = 32 * c + 8 * g;
-      v[u] = __builtin_amdgcn_raw_buffer_load_b128(abuf, c < cend ? (row * K + k) * 2 : kBufOOB, 0, kBufNT);
+      // plain load: the amax pass just read x, and part of it may still be cached
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(abuf, c < cend ? (row * K + k) * 2 : kBufOOB, 0, 0);
       if constexpr (SMOOTH) {
         sm[u][0] = __builtin_amdgcn_raw_buffer_load_b128(mbuf, c < cend ? k * 4 : kBufOOB, 0, 0);
         sm[u][1] = __builtin_amdgcn_raw_buffer_load_b128(mbuf, c < cend ? k * 4 + 16 : kBufOOB, 0, 0);
