@@ -178,24 +178,47 @@ hipError_t launch_running_amax(const void* x, bool bf16, int64_t n_elems, float*
 
 // ---------------------------------------------------------------- absmax quantizer
 
-// Load the 8 consecutive elements [8h, 8h+8) as fp32 (plain loads: measured
-// 5 % faster than non-temporal ones on this pass).
+// Grid cap of the absmax pass: 32768 workgroups of 256
+// lanes, one half block per lane for tensors up to 67 M elements (a
+// 14336 x 4096 weight then runs in a single iteration).  With a cap of 8192
+// (3.5 iterations a lane on that weight) the 8B layer set's absmax pass took
+// 184-190 us instead of 172-176.
+constexpr int64_t kQuantizeMaxGrid = 32768;
+
+// The raw bytes of half block h (elements [8h, 8h+8)): 16 bytes of bf16 or
+// 32 of fp32, plain loads (measured 5 % faster than non-temporal ones on
+// this pass), unpacked to fp32 once the next half block's loads are issued.
+struct Half8 {
+  u32x4 a, b;
+};
+
 template <bool kBF16>
-__device__ __forceinline__ void load8(const void* __restrict__ x, int64_t h, float w[8]) {
+__device__ __forceinline__ Half8 load_half8(const void* __restrict__ x, int64_t h) {
+  Half8 r;
   if constexpr (kBF16) {
-    u32x4 v = reinterpret_cast<const u32x4*>(x)[h];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      w[2 * j] = bf16_bits_to_f32(v[j] & 0xFFFFu);
-      w[2 * j + 1] = bf16_bits_to_f32(v[j] >> 16);
-    }
+    r.a = reinterpret_cast<const u32x4*>(x)[h];
+    r.b = u32x4{0u, 0u, 0u, 0u};
   } else {
     const u32x4* p = reinterpret_cast<const u32x4*>(x) + 2 * h;
-    u32x4 a = p[0], b = p[1];
+    r.a = p[0];
+    r.b = p[1];
+  }
+  return r;
+}
+
+template <bool kBF16>
+__device__ __forceinline__ void unpack_half8(const Half8& v, float w[8]) {
+  if constexpr (kBF16) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      w[j] = __uint_as_float(a[j]);
-      w[4 + j] = __uint_as_float(b[j]);
+      w[2 * j] = bf16_bits_to_f32(v.a[j] & 0xFFFFu);
+      w[2 * j + 1] = bf16_bits_to_f32(v.a[j] >> 16);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w[j] = __uint_as_float(v.a[j]);
+      w[4 + j] = __uint_as_float(v.b[j]);
     }
   }
 }
@@ -209,14 +232,23 @@ __global__ __launch_bounds__(256) void quantize_absmax_kernel(const void* __rest
                                                               const float* __restrict__ sg_ptr,
                                                               uint32_t* __restrict__ codes,
                                                               uint8_t* __restrict__ scales) {
+  // A lane's first half block is requested before anything else, and each
+  // iteration requests the next one before its own arithmetic (on the 8B
+  // layer set in fp32, with a grid of one half block per lane for most
+  // tensors: 196 -> 172-176 us).
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;  // a multiple of 64
+  int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  Half8 next{};
+  if (h < n_half) next = load_half8<kBF16>(x, h);
   const float sg = *sg_ptr;
   const float inv_sg = 1.0f / sg;
   const double six_sg = 6.0 * (double)sg;
   const bool pack = (reinterpret_cast<uintptr_t>(scales) & 3) == 0;
-  int64_t stride = (int64_t)gridDim.x * blockDim.x;  // a multiple of 64
-  for (int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; h < n_half; h += stride) {
+  for (; h < n_half; h += stride) {
+    const Half8 cur = next;
+    if (h + stride < n_half) next = load_half8<kBF16>(x, h + stride);
     float w[8];
-    load8<kBF16>(x, h, w);
+    unpack_half8<kBF16>(cur, w);
     float m = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(w[j]));
@@ -256,8 +288,10 @@ __global__ __launch_bounds__(256) void quantize_4o6_kernel(const void* __restric
   const bool odd = (threadIdx.x & 1) != 0;
   int64_t stride = (int64_t)gridDim.x * blockDim.x;  // a multiple of 64
   for (int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; h < n_half; h += stride) {
+    // (no load-ahead here: holding the next half block cost this
+    // register-heavy pass 2 % on the 8B layer set)
     float w[8];
-    load8<kBF16>(x, h, w);
+    unpack_half8<kBF16>(load_half8<kBF16>(x, h), w);
     float m = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(w[j]));
@@ -342,7 +376,7 @@ hipError_t launch_quantize_absmax(const void* x, bool bf16, int64_t n_elems, con
   int64_t n_half = n_elems / 8;
   if (n_half == 0) return hipSuccess;
   int64_t wg = (n_half + 255) / 256;
-  if (wg > 8192) wg = 8192;
+  if (wg > kQuantizeMaxGrid) wg = kQuantizeMaxGrid;
   if (bf16)
     hipLaunchKernelGGL(quantize_absmax_kernel<true>, dim3((unsigned)wg), dim3(256), 0, stream, x, n_half, sg,
                        reinterpret_cast<uint32_t*>(codes), scales);
