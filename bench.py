@@ -255,10 +255,12 @@ def main():
                 nbytes=M * K * 2 + N * K * 0.5625 + 2 * M * N)
 
     # The image and text streams of a double-stream DiT block are independent
-    # until the joint attention: their products run on two HIP streams (both
-    # at the default priority), forked from and joined back into the timed
-    # stream, so the short text-stream products fill CUs that the image
-    # stream's leave idle.
+    # until the joint attention, which needs both streams' q, k and v; the
+    # MLPs come after it.  Each phase runs the two streams' products on two
+    # HIP streams (both at the default priority), forked from and joined back
+    # into the timed stream.  In the MLP phase the image MLP-up product fills
+    # the chip, so the text MLP is queued behind it and runs beside the image
+    # MLP-down product, whose 192 tiles leave a quarter of the CUs idle.
     side = torch.cuda.Stream()
 
     def two_streams(run_img, run_txt):
@@ -267,6 +269,18 @@ def main():
         with torch.cuda.stream(side):
             run_txt()
         run_img()
+        main.wait_stream(side)
+
+    def dit_phases(img, txt):
+        """img, txt: (q/k/v products, MLP up, MLP down) of one stream each."""
+        two_streams(img[0], txt[0])
+        main = torch.cuda.current_stream()
+        img[1]()
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            txt[1]()
+            txt[2]()
+        img[2]()
         main.wait_stream(side)
 
     if "gemm" in phases or "dit" in phases:
@@ -290,14 +304,22 @@ def main():
                 dit_flops += 2.0 * ad.shape[0] * c.shape[0] * c.shape[1] * 2
 
         def dit_stream(ad, hd, w, ws_a, ws_h, outs):
-            nv.gemm_w4a4(ad, *w["to_q"], workspace=ws_a, out=outs["to_q"])
-            nv.gemm_w4a4(ad, *w["to_k"], workspace=ws_a, out=outs["to_k"], reuse_act=True)
-            nv.gemm_w4a4(ad, *w["to_v"], workspace=ws_a, out=outs["to_v"], reuse_act=True)
-            nv.gemm_w4a4(ad, *w["mlp_up"], workspace=ws_a, out=outs["mlp_up"])   # the MLP input is quantized anew
-            nv.gemm_w4a4(hd, *w["mlp_down"], workspace=ws_h, out=outs["mlp_down"])
+            def qkv():
+                nv.gemm_w4a4(ad, *w["to_q"], workspace=ws_a, out=outs["to_q"])
+                nv.gemm_w4a4(ad, *w["to_k"], workspace=ws_a, out=outs["to_k"], reuse_act=True)
+                nv.gemm_w4a4(ad, *w["to_v"], workspace=ws_a, out=outs["to_v"], reuse_act=True)
+
+            def up():   # the MLP input is quantized anew
+                nv.gemm_w4a4(ad, *w["mlp_up"], workspace=ws_a, out=outs["mlp_up"])
+
+            def down():
+                nv.gemm_w4a4(hd, *w["mlp_down"], workspace=ws_h, out=outs["mlp_down"])
+            return qkv, up, down
+
+        dit_img, dit_txt = dit_stream(*dit_calls[0]), dit_stream(*dit_calls[1])
 
         def dit_block():
-            two_streams(lambda: dit_stream(*dit_calls[0]), lambda: dit_stream(*dit_calls[1]))
+            dit_phases(dit_img, dit_txt)
 
         capture("gemm_dit_block", dit_block, flops=dit_flops)
 
@@ -378,15 +400,22 @@ def main():
 
         n_img = len(lora_calls) // 2   # the image stream's layers come first
 
-        def lora_layers(calls, svdq):
-            for act, wq, down, up, wsl, out, smooth in calls:
-                nv.gemm_w4a4(act, *wq, workspace=wsl, out=out, lora=(down, up), smooth=smooth if svdq else None)
+        def lora_layer(call, svdq):
+            act, wq, down, up, wsl, out, smooth = call
+            return lambda: nv.gemm_w4a4(act, *wq, workspace=wsl, out=out, lora=(down, up),
+                                        smooth=smooth if svdq else None)
+
+        def lora_stream(calls, svdq):   # (q/k/v, MLP up, MLP down) layers of one stream
+            return tuple(lora_layer(c, svdq) for c in calls)
+
+        lora_img, lora_txt = lora_stream(lora_calls[:n_img], False), lora_stream(lora_calls[n_img:], False)
+        svdq_img, svdq_txt = lora_stream(lora_calls[:n_img], True), lora_stream(lora_calls[n_img:], True)
 
         def dit_block_lora():
-            two_streams(lambda: lora_layers(lora_calls[:n_img], False), lambda: lora_layers(lora_calls[n_img:], False))
+            dit_phases(lora_img, lora_txt)
 
         def dit_block_svdq():
-            two_streams(lambda: lora_layers(lora_calls[:n_img], True), lambda: lora_layers(lora_calls[n_img:], True))
+            dit_phases(svdq_img, svdq_txt)
 
         capture("lora_dit_block", dit_block_lora, flops=lora_flops)
         capture("svdq_dit_block", dit_block_svdq, flops=lora_flops)
