@@ -583,7 +583,10 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu((B
   // bf16 output of a 256 x 256 tile with 16-byte aligned rows: each 128-row
   // half (the 4 waves with wm = h) goes through LDS (the free stages) and out
   // as 16-byte stores, 16 per lane instead of 128 two-byte ones (prefill
-  // 385-390 -> 384 us, DiT block 919-931 -> 912-914 us; same bytes).
+  // 385-390 -> 384 us, DiT block 919-931 -> 912-914 us; same bytes).  The
+  // stores are non-temporal: y is not read again here, and keeping it out of
+  // L2 leaves room for the A and W panels the other tiles share (prefill
+  // 383 -> 380-382 us, DiT block 915 -> 890-893 us).
   if constexpr (!SPLIT && BM == 256 && BN == 256 && WM == 2) {
     if (bf16_out && (N & 7) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0) {
       static_assert(sizeof(Stage) * 2 >= 128 * 256 * 2, "a half tile fits in two stages");
@@ -610,7 +613,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu((B
           const int row = tid / 32 + 16 * j, chunk = tid % 32;
           const int m = m0 + 128 * h + row, n = n0 + 8 * chunk;
           const u32x4 v = *reinterpret_cast<const u32x4*>(&half_tile[row * 256 + 8 * chunk]);
-          if (m < M && n < N) *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(y) + (int64_t)m * N + n) = v;
+          if (m < M && n < N) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(y) + (int64_t)m * N + n));
         }
         __syncthreads();
       }
