@@ -183,7 +183,10 @@ __global__ __launch_bounds__(NW * 64) void gemv_w4a16_kernel(const uint16_t* __r
         const int r = 4 * u + (lane >> 4);
         const int c = 4 * s0 + ((lane & 15) ^ r);
         const bool ok = c < 4 * send && c < nch;
-        buffer_to_lds16(cbuf, &lds_c[wave][t][64 * u], ok ? (16 * t + r) * half + 16 * c : kBufOOB, 0);
+        // non-temporal: each code byte is read once (decode calls on both
+        // shapes 1-5 % faster than with the temporal hint)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(cbuf, (__attribute__((address_space(3))) void*)&lds_c[wave][t][64 * u],
+                                                 16, ok ? (16 * t + r) * half + 16 * c : kBufOOB, 0, 0, kBufNT);
       }
     uint32_t pairs[T][4];
     // Lane (n, g) reads chunk 4 (s0 + u) + g of row n from slot (4 u + g) ^ n:
