@@ -238,7 +238,7 @@ __global__ __launch_bounds__(256) void act_sweep_kernel(const u32x4* __restrict_
     float mf = 0.0f;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const u32x4 v = __builtin_nontemporal_load(x + 2 * b + i);
+      const u32x4 v = x[2 * b + i];  // plain: the 4 candidate groups read the same blocks (316 -> 305 us)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         aw[8 * i + 2 * j] = fabsf(bf16_bits_to_f32(v[j] & 0xFFFFu));
