@@ -252,6 +252,71 @@ def test_mse_window_bounds_are_exact_e4m3_steps():
     assert oracle.mse_scale_code(blk, 1.0) == 0x38  # exact representation wins (zero error)
 
 
+def _random_f32_scales(seed, n):
+    """fp32 tensor scales with full 24-bit significands over many binades."""
+    g = inputs.rng(seed)
+    sig = g.integers(2 ** 23, 2 ** 24, n)
+    return [float(np.float32(np.ldexp(float(m), int(e)))) for m, e in zip(sig, g.integers(-40, -10, n))]
+
+
+def test_mse_candidate_union_at_the_e4m3_cap():
+    """Given s_g = 1 and max|W| = 6000, a = max|W| / (6 s_g) = 1000: the window
+    [a/2, min(2a, 448)] = [500, 448] holds no E4M3 value, so the absmax scale
+    (448, the saturated nearest value, byte 0x7E) is the only candidate
+    ("Tu pipeline NVFP4 ...", section 2, box on MSE vs absmax: the searched
+    scale is never worse than the absmax one, here because it is the absmax
+    one).  Without the absmax scale in the candidate set the search would
+    have no candidate at all."""
+    g = inputs.rng(61)
+    for i in range(24):
+        blk = (g.standard_normal(16) * 1000).astype(np.float32)
+        blk[i % 16] = np.float32(6000.0 if i % 2 == 0 else -6000.0)
+        if i >= 16:
+            blk *= np.float32(1 + i)          # a up to 25000: still only the capped absmax scale
+        sg = F(1)
+        code = oracle.mse_scale_code(blk, 1.0)
+        assert code == 0x7E, (i, code)
+        assert code == oracle.absmax_scale_code(blk, 1.0)
+        fb = [F(float(v)) for v in blk]
+        best, best_err, _, _ = exact.mse_search(fb, sg)
+        assert best == exact.E4M3[code] == 448
+        assert exact.block_error(fb, exact.E4M3[code], sg) <= exact.block_error(fb, exact.absmax_scale(fb, sg), sg)
+    # the same cap reached under a general s_g: max|W| = 1500 * 6 * s_g
+    for sg_f in _random_f32_scales(62, 8):
+        blk = (g.standard_normal(16) * 200 * sg_f).astype(np.float32)
+        blk[3] = np.float32(9000 * sg_f)
+        code = oracle.mse_scale_code(blk, sg_f)
+        fb = [F(float(v)) for v in blk]
+        best, _, _, _ = exact.mse_search(fb, F(sg_f))
+        assert code == 0x7E and best == 448, (sg_f, code)
+
+
+def test_mse_candidate_union_below_the_smallest_subnormal_scale():
+    """a = max|W| / (6 s_g) below 2^-10 (half the smallest positive E4M3 value
+    2^-9): the absmax scale rounds to 0 and the window [a/2, 2a] holds no
+    positive E4M3 value, so scale byte 0 (every code 0) is the only candidate
+    and the MSE search must return it."""
+    g = inputs.rng(63)
+    e4_min = 2.0 ** -9
+    for i, a_target in enumerate([2.0 ** -12, 2.0 ** -11, 0.9 * 2.0 ** -10, 0.999 * 2.0 ** -10, 1e-6, 2.0 ** -30]):
+        blk = (g.uniform(-1, 1, 16) * 6 * a_target).astype(np.float32)
+        blk[i] = np.float32(6 * a_target)
+        a = float(np.abs(blk).max()) / 6.0
+        assert 2 * a < e4_min                 # the window is empty
+        code = oracle.mse_scale_code(blk, 1.0)
+        assert code == 0 == oracle.absmax_scale_code(blk, 1.0), (a_target, code)
+        fb = [F(float(v)) for v in blk]
+        best, best_err, _, _ = exact.mse_search(fb, F(1))
+        assert best == 0 and best_err == exact.block_error(fb, F(0), F(1))
+    # and through the tensor entry point: scale bytes 0x00 and 0x7E, never 0xFF
+    rows = np.zeros((2, 16), dtype=np.float32)
+    rows[0, :] = np.float32(2.0 ** -13)
+    rows[1, 0] = np.float32(6000.0)
+    codes, scales, _ = oracle.quantize(rows, oracle.MSE, sg=1.0)
+    assert list(scales[:, 0]) == [0x00, 0x7E]
+    assert not codes[0].any()
+
+
 def test_worked_example_levels():
     # s_b * s_g = 0.01 with s_g = 0.01 given and s_b = 1.0 (E4M3 0x38)
     levels = sorted({float(r[0]) for r in _read("worked_example_scale_0p01.txt")})
@@ -336,6 +401,99 @@ def test_dot_products_small_integer_exact_and_numpy_crosscheck():
     ref = ah @ whh.T
     assert np.allclose(y.reshape(7, 9), ref, rtol=0, atol=1e-6 * (np.abs(ah) @ np.abs(whh).T).max())
     assert np.all(tau > 0)
+
+
+def _exact_dequant(codes, scales, sg, rows, cols):
+    """Exact rationals q * s_b * s_g, decoded with the exact checker's own
+    E2M1 and E4M3 tables (independent of the C oracle)."""
+    out = []
+    for r in range(rows):
+        row = []
+        for k in range(cols):
+            byte = int(codes[r, k // 2])
+            c = (byte >> 4) if k & 1 else (byte & 15)
+            mag = exact.E2M1_MAG[c & 7] * exact.E4M3[int(scales[r, k // 16])] * F(sg)
+            row.append(-mag if c & 8 else mag)
+        out.append(row)
+    return out
+
+
+def test_dequant_is_one_rounding_of_the_exact_product():
+    """W^ = q s_b s_g ("Tu pipeline NVFP4 ...", section 2, the hierarchical
+    reconstruction) rounded once to fp32: every code x every finite positive
+    scale byte x 128 fp32 tensor scales with full significands.  Rounding
+    s_b s_g to fp32 before the multiply by q (a double rounding) fails here."""
+    codes = np.tile(np.array([c | ((c + 1) << 4) for c in range(0, 16, 2)], dtype=np.uint8), (127, 1))
+    scales = np.arange(127, dtype=np.uint8).reshape(127, 1)
+    sgs = _random_f32_scales(64, 120) + [1.0, 0.01, 3.0 / 7.0, 1e-30, 2.0 ** 100,
+                                         float(np.nextafter(np.float32(1), np.float32(2)))]
+    for sg in (float(np.float32(v)) for v in sgs):
+        got = oracle.dequant(codes, scales, sg, 127, 16)
+        want = _exact_dequant(codes, scales, sg, 127, 16)
+        for r in range(127):
+            for k in range(16):
+                assert got[r, k] == float(exact.fp32(want[r][k])), (sg, r, k)
+
+
+def test_one_hot_products_equal_the_exact_dequantized_weight():
+    """A one-hot activation picks one weight element, whose exact value
+    q s_b s_g has at most 30 significant bits, so the fp64 product sum must
+    equal it exactly (rtol 0), and its tolerance must be 1e-5 |W^| rounded
+    once (the product tolerance at one nonzero term)."""
+    w = inputs.student_t_f32((6, 64), 65)
+    for sg in _random_f32_scales(66, 6) + [None]:
+        codes, scales, sgw = oracle.quantize(w, oracle.MSE, sg=sg)
+        want = _exact_dequant(codes, scales, sgw, 6, 64)
+        x = np.zeros((64, 64), dtype=np.float32)
+        x[np.arange(64), np.arange(64)] = 1.0
+        y, tau = oracle.dot_w4a16(x, codes, scales, sgw)
+        y, tau = y.reshape(64, 6), tau.reshape(64, 6)
+        for k in range(64):
+            for n in range(6):
+                assert y[k, n] == float(want[n][k]), (sg, k, n)
+                assert tau[k, n] == 1e-5 * abs(float(want[n][k])), (sg, k, n)
+        # W4A4: a one-hot activation block [6, 0, ...] quantizes exactly at
+        # s_gA = 1 (scale 1.0, code 6), so y* = 6 W^ exactly
+        a = np.zeros((16, 64), dtype=np.float32)
+        a[np.arange(16), 4 * np.arange(16)] = 6.0
+        ac, as_, _ = oracle.quantize(a, sg=1.0)
+        y4, t4 = oracle.dot_w4a4(ac, as_, 1.0, codes, scales, sgw, 64)
+        y4, t4 = y4.reshape(16, 6), t4.reshape(16, 6)
+        for m in range(16):
+            for n in range(6):
+                assert y4[m, n] == float(6 * want[n][4 * m])
+                assert t4[m, n] == 1e-5 * abs(float(6 * want[n][4 * m]))
+
+
+def test_product_tolerance_matches_exact_rational():
+    """tau = 1e-5 sum_k |a^_k| |w^_k| over the fully dequantized operands, and
+    y* = sum_k a^_k w^_k, recomputed in exact rationals from the exact
+    checker's decode (random operands, general tensor scales, W4A16 and
+    W4A4).  The fp64 sums may differ from the exact ones only by their
+    rounding (far below 1e-12 relative)."""
+    K = 96
+    g = inputs.rng(67)
+    w = (g.standard_t(5, (5, K)) * 0.02).astype(np.float32)
+    a = (g.standard_normal((4, K)) * np.where(g.uniform(size=K) < 0.1, 20.0, 1.0)).astype(np.float32)
+    xb = inputs.bf16_bits_to_f32(inputs.to_bf16_bits(a))
+    wc, ws, sgw = oracle.quantize(w, oracle.MSE)
+    ac, as_, sga = oracle.quantize(a)
+    W = _exact_dequant(wc, ws, sgw, 5, K)
+    A = _exact_dequant(ac, as_, sga, 4, K)
+    tol = F(1, 10 ** 12)
+    y16, t16 = oracle.dot_w4a16(xb, wc, ws, sgw)
+    y44, t44 = oracle.dot_w4a4(ac, as_, sga, wc, ws, sgw, K)
+    for m in range(4):
+        for n in range(5):
+            p = m * 5 + n
+            s = sum((F(float(xb[m, k])) * W[n][k] for k in range(K)), F(0))
+            t = F(1, 10 ** 5) * sum((abs(F(float(xb[m, k])) * W[n][k]) for k in range(K)), F(0))
+            assert abs(F(float(t16[p])) - t) <= tol * t, (m, n)
+            assert abs(F(float(y16[p])) - s) <= tol * t * 10 ** 5, (m, n)
+            s = sum((A[m][k] * W[n][k] for k in range(K)), F(0))
+            t = F(1, 10 ** 5) * sum((abs(A[m][k] * W[n][k]) for k in range(K)), F(0))
+            assert abs(F(float(t44[p])) - t) <= tol * t, (m, n)
+            assert abs(F(float(y44[p])) - s) <= tol * t * 10 ** 5, (m, n)
 
 
 def test_lora_term_numpy_crosscheck_and_tolerance_parts():
