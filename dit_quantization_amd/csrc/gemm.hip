@@ -388,25 +388,28 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu((B
   // 16 lanes (16 consecutive rows) at a time: rows 2j and 2j + 1 fall in the
   // two halves of the 64 banks and the 8 row pairs get 8 different chunks
   // (with the swizzle on row % 8, rows r and r + 8 collided: 2-way conflicts).
-  const __amdgpu_buffer_rsrc_t abuf = make_buf(a_hat + (int64_t)m0 * K, (uint32_t)(min(BM, M - m0) * K * 2));
+  // Panel bytes min(BM, M - m0) K 2 <= 256 * 2^22 * 2 = 2^31 (the largest K
+  // the C ABI admits): computed unsigned, every offset below stays under it.
+  const __amdgpu_buffer_rsrc_t abuf =
+      make_buf(a_hat + (int64_t)m0 * K, (uint32_t)min(BM, M - m0) * (uint32_t)K * 2u);
   uint32_t a_off[APT];
 #pragma unroll
   for (int j = 0; j < APT; ++j) {
     const int S = 64 * (wave * APT + j) + lane;
     const int r = S >> 3, c = (S & 7) ^ ((r >> 1) & 7);
-    a_off[j] = (uint32_t)((r * K + 8 * c) * 2);
+    a_off[j] = ((uint32_t)r * (uint32_t)K + 8u * (uint32_t)c) * 2u;
   }
   // W codes: slot u (= tid + NT j) holds row u / 2, half (u % 2) ^ ((row >> 3) & 1).
   // Scales: dword slot u holds bytes 2 (u % 2) .. +2 of row u / 2.
   const int w_rows = min(BN, N - n0);
-  const __amdgpu_buffer_rsrc_t wbuf = make_buf(codes + (int64_t)n0 * (K / 2), (uint32_t)(w_rows * (K / 2)));
-  const __amdgpu_buffer_rsrc_t sbuf = make_buf(scales + (int64_t)n0 * (K / 16), (uint32_t)(w_rows * (K / 16)));
+  const __amdgpu_buffer_rsrc_t wbuf = make_buf(codes + (int64_t)n0 * (K / 2), (uint32_t)w_rows * (uint32_t)(K / 2));
+  const __amdgpu_buffer_rsrc_t sbuf = make_buf(scales + (int64_t)n0 * (K / 16), (uint32_t)w_rows * (uint32_t)(K / 16));
   uint32_t w_off[WPT], s_off[WPT];
 #pragma unroll
   for (int j = 0; j < WPT; ++j) {
     const int u = tid + NT * j;
-    w_off[j] = (uint32_t)((u >> 1) * (K / 2) + 16 * ((u & 1) ^ ((u >> 4) & 1)));
-    s_off[j] = (uint32_t)((u >> 1) * (K / 16) + 2 * (u & 1));
+    w_off[j] = (uint32_t)(u >> 1) * (uint32_t)(K / 2) + 16u * (uint32_t)((u & 1) ^ ((u >> 4) & 1));
+    s_off[j] = (uint32_t)(u >> 1) * (uint32_t)(K / 16) + 2u * (uint32_t)(u & 1);
   }
 
   auto dma = [&](Stage& stg, int kt) {

@@ -11,7 +11,7 @@ namespace {
 
 using namespace nvfp4;
 
-constexpr int kVersion = 1 * 10000 + 5 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 6 * 100 + 0;
 static_assert(kSweepCandidates == NVFP4_SWEEP_CANDIDATES, "candidate count of the activation scale sweep");
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -29,6 +29,14 @@ size_t amax_ws_bytes(int64_t n, bool bf16) {
 void clear_error() { (void)hipGetLastError(); }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH; }
+
+// Calls are not graph-capture safe: refuse a stream that is being captured
+// (before anything is enqueued on it).
+int stream_status(hipStream_t s) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess) return NVFP4_ERR_LAUNCH;
+  return cs == hipStreamCaptureStatusNone ? NVFP4_OK : NVFP4_ERR_CAPTURE;
+}
 
 int validate_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, const uint8_t* codes,
                       const uint8_t* scales, const float* gs, int flags, const void* ws, size_t ws_bytes) {
@@ -56,6 +64,8 @@ int quantize_common(Search mode, const void* x, int x_dtype, int64_t rows, int64
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   bool bf16 = x_dtype == NVFP4_BF16;
   int64_t n = rows * cols;
+  if (n == 0 && (flags & NVFP4_GLOBAL_GIVEN)) return NVFP4_OK;  // nothing to write
+  if ((st = stream_status(s)) != NVFP4_OK) return st;
   clear_error();
   if ((flags & NVFP4_GLOBAL_GIVEN) == 0) {
     hipError_t e = launch_global_scale(x, bf16, n, reinterpret_cast<float*>(ws), gs, s);
@@ -74,6 +84,7 @@ size_t gemm_ws_bytes(int64_t M, int64_t K) {
 // The low-rank variant keeps L = x lora_down^T (bf16 [M, rank <= 128]) right
 // after the quantized activation and moves the amax partials behind it.
 constexpr int kMaxLoraRank = 128;
+constexpr int64_t kMaxGemmK = (int64_t)1 << 22;
 
 size_t lora_partial_bytes(int64_t M, int64_t K) {
   const int s = K > 0 ? lora_splits(M, K) : 1;
@@ -103,9 +114,10 @@ int gemm_common(const void* a, const float* a_global, const uint8_t* w_codes, co
   if (y_dtype != NVFP4_F32 && y_dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
   if (M < 0 || N < 0 || K < 0 || rank < 0 || !mul_ok(M, K) || !mul_ok(N, K) || !mul_ok(M, N)) return NVFP4_ERR_SHAPE;
   if (K % 16 != 0) return NVFP4_ERR_SHAPE;
-  // K <= 2^22: a 256-row operand panel (256 K 2 bytes) and its DMA offsets
-  // stay within the 32-bit buffer ranges the kernels address.
-  if (K % 64 != 0 || K == 0 || M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > (int64_t)1 << 22)
+  // K <= 2^22: a 256-row operand panel (256 K 2 bytes <= 2^31) and its DMA
+  // offsets stay within the 32-bit buffer ranges the kernels address.
+  static_assert((uint64_t)256 * ((uint64_t)1 << 22) * 2 <= ((uint64_t)1 << 31), "panel bytes fit 32 bits");
+  if (K % 64 != 0 || K == 0 || M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > kMaxGemmK)
     return NVFP4_ERR_UNSUPPORTED;
   if (lora && (rank % 16 != 0 || rank > kMaxLoraRank)) return NVFP4_ERR_UNSUPPORTED;
   if ((!reuse && !aligned(a, 16)) || !aligned(w_codes, 16) || !aligned(w_scales, 4) || !aligned(w_global, 4) ||
@@ -116,6 +128,7 @@ int gemm_common(const void* a, const float* a_global, const uint8_t* w_codes, co
   if (ws_bytes < (lora ? gemm_lora_ws_bytes(M, K) : gemm_ws_bytes(M, K))) return NVFP4_ERR_WORKSPACE;
   if (M == 0 || N == 0) return NVFP4_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (const int st = stream_status(s); st != NVFP4_OK) return st;
   char* ws = reinterpret_cast<char*>(workspace);
   float* sga = reinterpret_cast<float*>(ws);
   uint16_t* a_hat = reinterpret_cast<uint16_t*>(ws + 256);
@@ -172,6 +185,7 @@ const char* nvfp4_status_string(int status) {
     case NVFP4_ERR_UNSUPPORTED: return "shape outside the supported range (K % 32, M range)";
     case NVFP4_ERR_LAUNCH: return "HIP kernel launch failed";
     case NVFP4_ERR_FLAGS: return "unknown flag bits";
+    case NVFP4_ERR_CAPTURE: return "the stream is being captured into a HIP graph; calls are not capture-safe";
     default: return "unknown status";
   }
 }
@@ -223,6 +237,8 @@ int nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const float* glob
   if (cols % 16 != 0) return NVFP4_ERR_SHAPE;
   if (cols % 32 != 0) return NVFP4_ERR_UNSUPPORTED;
   if (!aligned(codes, 4) || !aligned(global_scale, 4) || !aligned(out, 16)) return NVFP4_ERR_ALIGN;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  if (const int st = stream_status(reinterpret_cast<hipStream_t>(stream)); st != NVFP4_OK) return st;
   clear_error();
   return launch_status(launch_dequant(codes, scales, global_scale, rows * cols, out, out_dtype == NVFP4_BF16,
                                       reinterpret_cast<hipStream_t>(stream)));
@@ -246,6 +262,7 @@ int nvfp4_gemv_w4a16(const void* x, const uint8_t* w_codes, const uint8_t* w_sca
   const int splits = gemv_splits(M, N, K);
   float* partial = (splits > 1 && workspace && ws_bytes >= (size_t)splits * M * N * 4)
                        ? reinterpret_cast<float*>(workspace) : nullptr;
+  if (const int st = stream_status(reinterpret_cast<hipStream_t>(stream)); st != NVFP4_OK) return st;
   clear_error();
   return launch_status(launch_gemv_w4a16(reinterpret_cast<const uint16_t*>(x), w_codes, w_scales, w_global, M, N,
                                          K, y, y_dtype == NVFP4_BF16, partial,
@@ -286,6 +303,8 @@ int nvfp4_channel_amax(const void* x, int x_dtype, int64_t rows, int64_t cols, f
   if (rows < 0 || cols < 0 || !mul_ok(rows, cols) || cols % 16 != 0) return NVFP4_ERR_SHAPE;
   if (cols > (int64_t)1 << 30) return NVFP4_ERR_UNSUPPORTED;
   if (!aligned(x, 16) || !aligned(amax, 4)) return NVFP4_ERR_ALIGN;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  if (const int st = stream_status(reinterpret_cast<hipStream_t>(stream)); st != NVFP4_OK) return st;
   clear_error();
   return launch_status(launch_channel_amax(x, x_dtype == NVFP4_BF16, rows, cols, amax,
                                            reinterpret_cast<hipStream_t>(stream)));
@@ -299,6 +318,7 @@ int nvfp4_act_amax(const void* x, int x_dtype, int64_t rows, int64_t cols, float
   if (!aligned(x, 16) || !aligned(amax, 4)) return NVFP4_ERR_ALIGN;
   if (ws_bytes < calibrate_ws_bytes(rows * cols)) return NVFP4_ERR_WORKSPACE;
   if (rows == 0 || cols == 0) return NVFP4_OK;
+  if (const int st = stream_status(reinterpret_cast<hipStream_t>(stream)); st != NVFP4_OK) return st;
   clear_error();
   return launch_status(launch_running_amax(x, x_dtype == NVFP4_BF16, rows * cols, reinterpret_cast<float*>(workspace),
                                            amax, reinterpret_cast<hipStream_t>(stream)));
@@ -311,6 +331,7 @@ int nvfp4_act_scale_sweep(const void* x, int64_t rows, int64_t cols, const float
   if (!aligned(x, 16) || !aligned(amax, 4) || !aligned(errors, 8) || !aligned(scale, 4) || !aligned(workspace, 256))
     return NVFP4_ERR_ALIGN;
   if (ws_bytes < calibrate_ws_bytes(rows * cols)) return NVFP4_ERR_WORKSPACE;
+  if (const int st = stream_status(reinterpret_cast<hipStream_t>(stream)); st != NVFP4_OK) return st;
   clear_error();
   return launch_status(launch_act_scale_sweep(reinterpret_cast<const uint16_t*>(x), rows * cols, amax,
                                               reinterpret_cast<double*>(workspace), errors, scale,

@@ -125,3 +125,33 @@ def lora_factors(r, K, N, seed, up_std=0.03):
     down = normal_f32((r, K), seed, std=1.0 / np.sqrt(K))
     up = normal_f32((N, r), seed + 1, std=up_std)
     return to_bf16_bits(down), to_bf16_bits(up)
+
+
+def random_bf16_bits(shape, seed):
+    """bf16 bit patterns with a random sign, a random 7-bit mantissa and one
+    of four exponents (magnitudes in [1/8, 4)): every element random, drawn
+    in row chunks so large edge-case operands stay cheap to make."""
+    g = rng(seed)
+    out = np.empty(shape, dtype=np.uint16)
+    rows = shape[0]
+    step = max(1, (1 << 26) // max(1, int(np.prod(shape[1:]))))
+    for r0 in range(0, rows, step):
+        r = g.integers(0, 1 << 16, size=(min(step, rows - r0),) + tuple(shape[1:]), dtype=np.uint16)
+        o = out[r0:r0 + r.shape[0]]
+        np.bitwise_and(r, 0x807F, out=o)        # sign and mantissa
+        r >>= 7
+        r &= 3
+        r += 124                                # exponent 124 .. 127
+        r <<= 7
+        o |= r
+    return out
+
+
+def random_nvfp4_weight(rows, cols, seed):
+    """An NVFP4 weight made of random code bytes, random E4M3 scale bytes in
+    0x28..0x47 (0.125 .. 1.875) and a tensor scale 1/2688: (codes [rows,
+    cols/2] u8, scales [rows, cols/16] u8, s_g)."""
+    g = rng(seed)
+    codes = g.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    scales = g.integers(0x28, 0x48, size=(rows, cols // 16), dtype=np.uint8)
+    return codes, scales, float(np.float32(1.0 / 2688.0))

@@ -13,7 +13,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_LAUNCH, ERR_FLAGS = range(9)
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_LAUNCH, ERR_FLAGS, ERR_CAPTURE = (
+    range(10))
 F32, BF16 = 0, 1
 GLOBAL_COMPUTE, GLOBAL_GIVEN = 0, 1
 OP_QUANTIZE, OP_GEMM_W4A4, OP_GEMV_W4A16, OP_GEMM_W4A4_LORA, OP_ACT_CALIBRATE, OP_GEMM_W4A4_SPLITK = (
@@ -101,6 +102,10 @@ def _need_cuda(*ts):
     for t in ts:
         if t is not None and (not t.is_cuda or not t.is_contiguous()):
             raise ValueError("tensors must be contiguous and on the GPU")
+    if torch.cuda.is_current_stream_capturing():
+        # The library refuses a capturing stream too (NVFP4_ERR_CAPTURE); this
+        # raises before any per-call workspace is allocated.
+        raise RuntimeError("nvfp4 calls are not graph-capture safe: the current stream is being captured")
 
 
 def _alloc_ws(nbytes, device):

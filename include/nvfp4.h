@@ -49,7 +49,11 @@
  *   - the fast path requires cols (K) % 32 == 0 and 16-byte aligned
  *     pointers (4-byte for scales, global scale and 1-row outputs);
  *     otherwise NVFP4_ERR_UNSUPPORTED / NVFP4_ERR_ALIGN is returned;
- *   - non-finite inputs are a caller error: the outputs are unspecified.
+ *   - non-finite inputs are a caller error: the outputs are unspecified;
+ *   - calls are NOT graph-capture safe: after the arguments are validated,
+ *     every call that would launch asks the runtime whether `stream` is
+ *     being captured and, if so, returns NVFP4_ERR_CAPTURE without
+ *     launching (NVFP4_ERR_LAUNCH if the runtime cannot tell).
  */
 #ifndef NVFP4_H_
 #define NVFP4_H_
@@ -70,7 +74,8 @@ typedef enum {
   NVFP4_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than nvfp4_workspace_bytes */
   NVFP4_ERR_UNSUPPORTED = 6, /* valid NVFP4 shape outside the kernels' range (K % 32, M > 16, ...) */
   NVFP4_ERR_LAUNCH = 7,      /* the HIP runtime reported an error at launch */
-  NVFP4_ERR_FLAGS = 8        /* unknown flag bits */
+  NVFP4_ERR_FLAGS = 8,       /* unknown flag bits */
+  NVFP4_ERR_CAPTURE = 9      /* `stream` is being captured into a HIP graph (calls are not capture-safe) */
 } nvfp4_status;
 
 typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1 } nvfp4_dtype;

@@ -209,6 +209,36 @@ def dot_w4a4(a_codes, a_scales, sga, w_codes, w_scales, sgw, K, pairs=None, M=No
     return y, tau
 
 
+def dot_w4a4_matmul(a_codes, a_scales, sga, w_codes, w_scales, sgw, K):
+    """y* and tau for every (m, n) of the given operand rows, by the same
+    definition as dot_w4a4 ("NVFP4 en difusion ...", section 2: out =
+    (A s_a)(B s_b)^T; fp64 sums, tau = 1e-5 sum_k |a^||w^|), with a float64
+    matrix product (a library primitive) taking the K-sums.  The operands
+    are the oracle's dequant at s_g = 1: the exact values q s_b (at most 6
+    significant bits, magnitudes 2^-10 .. 2688, exact in fp32); every product
+    is exact in fp64 and the exact fp64 product s_gA s_gW scales the sums.
+    Only the order of the fp64 additions differs from dot_w4a4, which keeps
+    the two within about K 2^-53 sum |a^||w^| of each other."""
+    M, N = a_scales.shape[0], w_scales.shape[0]
+    A = dequant(a_codes, a_scales, 1.0, M, K).astype(np.float64)
+    W = dequant(w_codes, w_scales, 1.0, N, K).astype(np.float64)
+    g = float(np.float32(sga)) * float(np.float32(sgw))
+    y = (A @ W.T) * g
+    tau = 1e-5 * ((np.abs(A) @ np.abs(W).T) * g)
+    return y, tau
+
+
+def dot_w4a16_matmul(x, w_codes, w_scales, sgw):
+    """W4A16 counterpart of dot_w4a4_matmul: y* = s_gW x (q_w s_w)^T and
+    tau = 1e-5 |x| |w^|^T for bf16 x [M, K] given as float32 (products of
+    a bf16 and a q s_b value have at most 14 significant bits: exact)."""
+    x = _as_f32_2d(x).astype(np.float64)
+    N = w_scales.shape[0]
+    W = dequant(w_codes, w_scales, 1.0, N, x.shape[1]).astype(np.float64)
+    g = float(np.float32(sgw))
+    return (x @ W.T) * g, 1e-5 * ((np.abs(x) @ np.abs(W).T) * g)
+
+
 def lora_term(x, A, B, pairs=None, threads=None):
     """fp64 low-rank term y*_L[m,n] = sum_j (x A^T)[m,j] B[n,j] and its
     tolerance for the requested (m, n) pairs (all pairs if None).  x [M, K],

@@ -32,8 +32,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert nv.lib().nvfp4_version() == 10500
-    for s in range(9):
+    assert nv.lib().nvfp4_version() == 10600
+    for s in range(10):
         assert nv.status_string(s) and nv.status_string(s) != "unknown status"
     assert nv.status_string(99) == "unknown status"
 

@@ -200,40 +200,90 @@ def test_gemm_dit_block_sampled():
                         what=f"dit stream{stream} {name}")
 
 
-@pytest.mark.parametrize("mnk", [(70, 130, 1024), (300, 520, 4096), (33, 96, 4096), (100, 200, 1344),
-                                 (512, 3072, 3072)])
-def test_gemm_splitk_matches_oracle(mnk):
-    """Short activations split K over workgroups when the workspace holds the
-    partial sums; both the split and the unsplit product must meet tau, and
-    the split one must repeat bit for bit."""
+def _run_splitk(mnk, seed):
+    """Product on a workspace with room for the split-K partial sums (filled
+    with 0xFF bytes, NaN as fp32, before the call) and on one without.
+    Returns the host copies and the partial region as fp32 after the call."""
     M, N, K = mnk
-    print(f"[case] gemm split-K M={M} N={N} K={K}", flush=True)
-    assert nv.workspace_bytes(nv.OP_GEMM_W4A4_SPLITK, M, N) > 0
-    a = inputs.normal_f32((M, K), M + 31)
-    a, _ = inputs.with_outlier_columns(a, max(1, K // 100), 32)
+    a = inputs.normal_f32((M, K), M + seed)
+    a, _ = inputs.with_outlier_columns(a, max(1, K // 100), seed + 1)
     ab = inputs.to_bf16_bits(a)
-    c, s, g = _quant_weight(inputs.student_t_f32((N, K), N + 33), oracle.MSE if N * K <= 1 << 22 else oracle.ABSMAX)
+    c, s, g = _quant_weight(inputs.student_t_f32((N, K), N + seed + 2),
+                            oracle.MSE if N * K <= 1 << 22 else oracle.ABSMAX)
     a_dev = dev_bf16(ab)
-    ws_split = torch.empty(nv.gemm_workspace_bytes(M, N, K), dtype=torch.uint8, device=DEV)
+    base = nv.workspace_bytes(nv.OP_GEMM_W4A4, M, K)
+    ws_split = torch.full((nv.gemm_workspace_bytes(M, N, K),), 0xFF, dtype=torch.uint8, device=DEV)
     ws_plain = torch.empty(nv.gemm_workspace_bytes(M, N, K, split_k=False), dtype=torch.uint8, device=DEV)
     y_split = nv.gemm_w4a4(a_dev, c, s, g, out_dtype=torch.float32, workspace=ws_split)
+    region = host(ws_split)[base:].view(np.float32).copy()
     y_plain = nv.gemm_w4a4(a_dev, c, s, g, out_dtype=torch.float32, workspace=ws_plain)
     yb_split = nv.gemm_w4a4(a_dev, c, s, g, workspace=ws_split)
+    y_again = nv.gemm_w4a4(a_dev, c, s, g, out_dtype=torch.float32, workspace=ws_split)
     torch.cuda.synchronize()
     ac, as_, asg = oracle.quantize(inputs.bf16_bits_to_f32(ab), oracle.ABSMAX)
     oc, os_, og = _oracle_weight(c)
-    if M * N > 200000:
-        pairs = _sample_pairs(M, N, 4000, 5)
-        ystar, tau = oracle.dot_w4a4(ac, as_, asg, oc, os_, og, K, pairs=pairs, M=M, N=N)
-        sel = (pairs[0], pairs[1])
-    else:
-        ystar, tau = oracle.dot_w4a4(ac, as_, asg, oc, os_, og, K)
-        sel = slice(None)
-    assert_within_tau(host(y_split)[sel].reshape(-1), ystar, tau, "split fp32")
-    assert_within_tau(host(y_plain)[sel].reshape(-1), ystar, tau, "plain fp32")
-    assert_bracket_bf16(host(yb_split)[sel].reshape(-1), ystar, tau, "split bf16")
-    y_again = nv.gemm_w4a4(a_dev, c, s, g, out_dtype=torch.float32, workspace=ws_split)
-    assert np.array_equal(host(y_again), host(y_split))
+    return (host(y_split), host(y_plain), host(yb_split), host(y_again), region,
+            (ac, as_, asg, oc, os_, og))
+
+
+@pytest.mark.parametrize("mnk,ranges", [((300, 520, 4096), 2), ((33, 96, 4096), 2), ((40, 200, 8192), 4),
+                                        ((512, 3072, 12288), 4)])
+def test_gemm_splitk_matches_oracle(mnk, ranges):
+    """Short activations split K over workgroups when the workspace holds the
+    partial sums (at least 32 K steps of 64 per range, at most 8 ranges).
+    The partial region must have been written (so the split ran), every
+    output of the split and the unsplit product must meet tau against the
+    oracle (full compare, through the float64 matrix-product form of the
+    definition), and the split product must repeat bit for bit.  512 x 3072 x
+    12288 is the text-stream MLP-down product of the DiT block, 4 ranges."""
+    M, N, K = mnk
+    print(f"[case] gemm split-K M={M} N={N} K={K}", flush=True)
+    assert nv.workspace_bytes(nv.OP_GEMM_W4A4_SPLITK, M, N) >= ranges * M * N * 4
+    y_split, y_plain, yb_split, y_again, region, (ac, as_, asg, oc, os_, og) = _run_splitk(mnk, 31)
+    assert np.isfinite(region[:ranges * M * N]).all()
+    ystar, tau = oracle.dot_w4a4_matmul(ac, as_, asg, oc, os_, og, K)
+    assert_within_tau(y_split.reshape(-1), ystar.reshape(-1), tau.reshape(-1), "split fp32")
+    assert_within_tau(y_plain.reshape(-1), ystar.reshape(-1), tau.reshape(-1), "plain fp32")
+    assert_bracket_bf16(yb_split.reshape(-1), ystar.reshape(-1), tau.reshape(-1), "split bf16")
+    assert np.array_equal(y_again, y_split)
+
+
+@pytest.mark.parametrize("mnk", [(70, 130, 1024), (100, 200, 1344), (512, 3072, 3072)])
+def test_gemm_short_k_stays_unsplit(mnk):
+    """Short activations whose K gives fewer than 32 K steps per range (the
+    DiT text-stream q/k/v product 512 x 3072 x 3072 among them) run unsplit
+    even with the partials' room in the workspace: the region stays
+    untouched and the outputs meet tau."""
+    M, N, K = mnk
+    print(f"[case] gemm no split M={M} N={N} K={K}", flush=True)
+    y_split, y_plain, yb_split, y_again, region, (ac, as_, asg, oc, os_, og) = _run_splitk(mnk, 41)
+    if region.size:
+        assert np.all(region.view(np.uint32) == 0xFFFFFFFF)
+    ystar, tau = oracle.dot_w4a4_matmul(ac, as_, asg, oc, os_, og, K)
+    assert_within_tau(y_split.reshape(-1), ystar.reshape(-1), tau.reshape(-1), "fp32")
+    assert np.array_equal(y_split, y_plain)
+    assert_bracket_bf16(yb_split.reshape(-1), ystar.reshape(-1), tau.reshape(-1), "bf16")
+
+
+def test_gemm_prefill_row_band():
+    """A fixed 256-row band of the prefill product (rows 1024..1279, one full
+    row of 256 x 256 tiles: all 56 column tiles) against the oracle, every
+    output (the float64 matrix-product form of the definition)."""
+    ab = inputs.prefill_activation()
+    (_, w), = list(inputs.layerset(["gate"]))
+    c, s, g = _quant_weight(w)
+    del w
+    M, K = ab.shape
+    N = c.shape[0]
+    print(f"[case] gemm prefill band M={M} N={N} K={K}", flush=True)
+    y32 = host(nv.gemm_w4a4(dev_bf16(ab), c, s, g, out_dtype=torch.float32))
+    yb = host(nv.gemm_w4a4(dev_bf16(ab), c, s, g))
+    ac, as_, asg = oracle.quantize(inputs.bf16_bits_to_f32(ab), oracle.ABSMAX)
+    oc, os_, og = _oracle_weight(c)
+    band = slice(1024, 1280)
+    ystar, tau = oracle.dot_w4a4_matmul(ac[band], as_[band], asg, oc, os_, og, K)
+    assert_within_tau(y32[band].reshape(-1), ystar.reshape(-1), tau.reshape(-1), "band fp32")
+    assert_bracket_bf16(yb[band].reshape(-1), ystar.reshape(-1), tau.reshape(-1), "band bf16")
 
 
 def test_gemm_and_gemv_deterministic():
@@ -282,8 +332,8 @@ def test_gemv_maximum_k(M):
 
 
 def test_gemm_maximum_k():
-    """K = 2^22, the largest the W4A4 product accepts (M = N = 16), split into
-    8 K ranges and unsplit."""
+    """K = 2^22, the largest the W4A4 product accepts, on 128 x 128 tiles
+    (M = N = 16), split into 8 K ranges and unsplit."""
     M, N, K = 16, 16, 1 << 22
     print(f"[case] gemm max K M={M} N={N} K={K}", flush=True)
     ab = inputs.to_bf16_bits(inputs.normal_f32((M, K), 78))
@@ -297,3 +347,34 @@ def test_gemm_maximum_k():
         ws = torch.empty(nv.gemm_workspace_bytes(M, N, K, split_k=split), dtype=torch.uint8, device=DEV)
         y32 = host(nv.gemm_w4a4(a_dev, c, s, g, out_dtype=torch.float32, workspace=ws))
         assert_within_tau(y32.reshape(-1), ystar, tau, f"max K split={split}")
+
+
+def test_gemm_maximum_k_256_row_panels():
+    """K = 2^22 on the 256 x 256 tiles (M = 1024, N = 8192: 128 tiles, the
+    fewest that select them), whose 256-row activation panel spans 2^31
+    bytes, the edge of the kernels' 32-bit buffer ranges.  The activation is
+    random bf16 everywhere (so a wrapped offset would read other data); the
+    weight repeats a random 256-row block down its rows.  Sampled outputs in
+    every 256-row panel against the oracle."""
+    M, N, K = 1024, 8192, 1 << 22
+    print(f"[case] gemm max K 256-row panels M={M} N={N} K={K}", flush=True)
+    ab = inputs.random_bf16_bits((M, K), 85)
+    wc, ws_, sgw = inputs.random_nvfp4_weight(256, K, 86)
+    amax_bits = max(int((ab[i:i + 64] & 0x7FFF).max()) for i in range(0, M, 64))   # |bf16| orders as its bits
+    amax = float(inputs.bf16_bits_to_f32(np.array([amax_bits], dtype=np.uint16))[0])
+    asg = oracle.global_scale(amax)
+    rows = np.array([0, 255, 256, 700, 768, 1023], dtype=np.int64)
+    ac, as_, _ = oracle.quantize(inputs.bf16_bits_to_f32(ab[rows]), oracle.ABSMAX, sg=asg)
+    a_dev = dev_bf16(ab)
+    del ab
+    c = torch.from_numpy(wc).to(DEV).repeat(N // 256, 1)
+    s = torch.from_numpy(ws_).to(DEV).repeat(N // 256, 1)
+    g = torch.tensor([sgw], dtype=torch.float32, device=DEV)
+    y = host(nv.gemm_w4a4(a_dev, c, s, g, out_dtype=torch.float32))
+    del a_dev, c, s
+    torch.cuda.empty_cache()
+    cols = np.array([0, 255, 256, 4095, 4096, 8191, 5000, 777], dtype=np.int64)
+    pm, pn = np.meshgrid(np.arange(rows.size), cols, indexing="ij")
+    pm, pn = pm.reshape(-1), pn.reshape(-1)
+    ystar, tau = oracle.dot_w4a4(ac, as_, asg, wc, ws_, sgw, K, pairs=(pm, pn % 256), M=rows.size, N=256)
+    assert_within_tau(y[rows[pm], pn], ystar, tau, "max K 256-row panels")

@@ -126,3 +126,71 @@ def test_svdq_beats_plain_w4a4_on_outlier_activations():
     e_plain = np.linalg.norm(y_plain - y_ref) / np.linalg.norm(y_ref)
     print(f"relative error: plain W4A4 {e_plain:.4f}, SVDQuant r={r} {e_svdq:.4f}", flush=True)
     assert e_svdq < 0.8 * e_plain
+
+
+def _dit_layer(stream, li):
+    """The benchmark's SVDQuant DiT layer `li` (q/k/v fused, MLP up, MLP down)
+    of stream 0 (image, M = 4096) or 1 (text, M = 512): activation bf16 bits,
+    fp32 weight, and the rank-32 low-rank factors the benchmark draws."""
+    a_img, a_txt, h_img, h_txt = inputs.dit_activations()
+    a, h = (a_img, h_img) if stream == 0 else (a_txt, h_txt)
+    raw = dict(inputs.dit_weights(stream))
+    w, act = [(np.concatenate([raw["to_q"], raw["to_k"], raw["to_v"]]), a), (raw["mlp_up"], a),
+              (raw["mlp_down"], h)][li]
+    N, K = w.shape
+    down, up = inputs.lora_factors(32, K, N, 300 + 10 * stream + li)
+    return act, w, down, up
+
+
+@pytest.mark.parametrize("stream,li", [(0, 0), (0, 1), (0, 2), (1, 0), (1, 1), (1, 2)])
+def test_svdq_dit_block_layers_sampled(stream, li):
+    """Every SVDQuant layer of the DiT block stage at its own shape (image
+    M = 4096 / text M = 512; q/k/v 9216 x 3072, MLP up 12288 x 3072, MLP down
+    3072 x 12288; rank 32; smoothing from the activation's channel ranges):
+    the smoothed activation's quantization bit-exact in the workspace (whole
+    tensor), L on 64 rows, y on 600 sampled outputs plus the corners."""
+    ab, w, down_b, up_b = _dit_layer(stream, li)
+    M, K = ab.shape
+    N, r = w.shape[0], down_b.shape[0]
+    print(f"[case] svdq dit stream={stream} layer={li} M={M} N={N} K={K} r={r}", flush=True)
+    x32 = inputs.bf16_bits_to_f32(ab)
+    a_k = np.abs(x32).max(axis=0)
+    w_k = np.abs(w).max(axis=0)
+    lam, mult = oracle.smooth_factors(a_k, w_k)
+    assert np.array_equal(svdquant.smoothing(a_k, w_k)[1], mult)     # the host preparation's multipliers
+    oc, os_, og = oracle.quantize(w, oracle.ABSMAX)
+    del w
+    c, s = torch.from_numpy(oc).to(DEV), torch.from_numpy(os_).to(DEV)
+    g = torch.tensor([og], dtype=torch.float32, device=DEV)
+    ws = torch.empty(nv.workspace_bytes(nv.OP_GEMM_W4A4_LORA, M, K), dtype=torch.uint8, device=DEV)
+    a_dev, down, up = dev_bf16(ab), dev_bf16(down_b), dev_bf16(up_b)
+    smooth = torch.from_numpy(mult).to(DEV)
+    y32 = host(nv.gemm_w4a4(a_dev, c, s, g, out_dtype=torch.float32, workspace=ws, lora=(down, up), smooth=smooth))
+    wsh = host(ws)
+    yb = host(nv.gemm_w4a4(a_dev, c, s, g, workspace=ws, lora=(down, up), smooth=smooth))
+    xs = oracle.smooth_act(x32, mult)
+    del x32
+    ac, as_, asg = oracle.quantize(xs, oracle.ABSMAX)
+    assert wsh[:4].view(np.float32)[0] == np.float32(asg)
+    ahat = wsh[256:256 + 2 * M * K].view(np.float16).reshape(M, K)
+    assert np.array_equal(ahat.astype(np.float32), oracle.dequant(ac, as_, 1.0, M, K))
+    del ahat
+    downf, upf = inputs.bf16_bits_to_f32(down_b), inputs.bf16_bits_to_f32(up_b)
+    off = nv.gemm_lora_l_offset(M, K)
+    L = wsh[off:off + 2 * M * r].view(np.uint16).reshape(M, r)
+    lrows = inputs.rng(90 + 3 * stream + li).choice(M, 64, replace=False)
+    lm, lj = np.meshgrid(lrows, np.arange(r), indexing="ij")
+    lstar, ltau = oracle.lora_term(xs, downf, np.eye(r, dtype=np.float32), pairs=(lm.reshape(-1), lj.reshape(-1)))
+    assert_within_tau(inputs.bf16_bits_to_f32(L[lm, lj]).reshape(-1), lstar, ltau, "L")
+    pm, pn = _sample_pairs(M, N, 600, 95 + 3 * stream + li)
+    ystar, tau = oracle.dot_w4a4(ac, as_, asg, oc, os_, og, K, pairs=(pm, pn), M=M, N=N)
+    lst, lt = oracle.lora_term(xs, downf, upf, pairs=(pm, pn))
+    assert_within_tau(y32[pm, pn], ystar + lst, tau + lt, "fp32")
+    assert_bracket_bf16(yb[pm, pn], ystar + lst, tau + lt, "bf16")
+
+
+def _sample_pairs(M, N, n, seed):
+    g = inputs.rng(seed)
+    pm = np.concatenate([[0, M - 1, 0, M - 1], g.integers(0, M, n)])
+    pn = np.concatenate([[0, 0, N - 1, N - 1], g.integers(0, N, n)])
+    return pm.astype(np.int64), pn.astype(np.int64)

@@ -496,6 +496,30 @@ def test_product_tolerance_matches_exact_rational():
             assert abs(F(float(y44[p])) - s) <= tol * t * 10 ** 5, (m, n)
 
 
+def test_matmul_products_agree_with_the_sequential_oracle():
+    """The matrix-product form of the W4A4 / W4A16 definitions (float64
+    library matmul over the exactly decoded operands) agrees with the
+    sequential fp64 dot products to fp64 rounding, at general tensor scales
+    and over several 256-wide tiles plus a ragged tail."""
+    M, N, K = 37, 300, 1088
+    a = inputs.normal_f32((M, K), 81)
+    a, _ = inputs.with_outlier_columns(a, 11, 82)
+    w = inputs.student_t_f32((N, K), 83)
+    ac, as_, sga = oracle.quantize(a)
+    wc, ws, sgw = oracle.quantize(w, oracle.MSE)
+    y, tau = oracle.dot_w4a4(ac, as_, sga, wc, ws, sgw, K)
+    ym, taum = oracle.dot_w4a4_matmul(ac, as_, sga, wc, ws, sgw, K)
+    y, tau = y.reshape(M, N), tau.reshape(M, N)
+    assert np.all(np.abs(ym - y) <= 1e-12 * tau / 1e-5)
+    assert np.allclose(taum, tau, rtol=1e-12, atol=0)
+    xb = inputs.bf16_bits_to_f32(inputs.to_bf16_bits(a))
+    y16, t16 = oracle.dot_w4a16(xb, wc, ws, sgw)
+    y16m, t16m = oracle.dot_w4a16_matmul(xb, wc, ws, sgw)
+    y16, t16 = y16.reshape(M, N), t16.reshape(M, N)
+    assert np.all(np.abs(y16m - y16) <= 1e-12 * t16 / 1e-5)
+    assert np.allclose(t16m, t16, rtol=1e-12, atol=0)
+
+
 def test_lora_term_numpy_crosscheck_and_tolerance_parts():
     rng = np.random.default_rng(11)
     M, K, r, N = 5, 96, 16, 7
