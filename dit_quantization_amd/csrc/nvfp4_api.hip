@@ -5,13 +5,23 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "kernels.hpp"
+
+// Fixed scratch of nvfp4_gemm_w4a4_noalloc: one copy on every GPU the
+// library runs on, held until the process ends.  In host code this name is
+// only a stand-in for the symbol: kernels and copies get the device address
+// that hipGetSymbolAddress returns for the current device (see
+// noalloc_scratch below), never the name itself.
+static __device__ __align__(256) unsigned char scratch[NVFP4_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
 using namespace nvfp4;
 
-constexpr int kVersion = 1 * 10000 + 6 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 7 * 100 + 0;
 static_assert(kSweepCandidates == NVFP4_SWEEP_CANDIDATES, "candidate count of the activation scale sweep");
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -29,6 +39,28 @@ size_t amax_ws_bytes(int64_t n, bool bf16) {
 void clear_error() { (void)hipGetLastError(); }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH; }
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return NVFP4_ERR_LAUNCH;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return NVFP4_ERR_LAUNCH;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return NVFP4_OK;
+}
 
 // Calls are not graph-capture safe: refuse a stream that is being captured
 // (before anything is enqueued on it).
@@ -102,13 +134,16 @@ size_t calibrate_ws_bytes(int64_t n) {
   return amax > sweep ? amax : sweep;
 }
 
+// use_scratch: the allocation-free variant; `workspace` and `ws_bytes` are
+// ignored and the call runs on the fixed per-device scratch.
 int gemm_common(const void* a, const float* a_global, const uint8_t* w_codes, const uint8_t* w_scales,
                 const float* w_global, const float* smooth, const void* lora_down, const void* lora_up, int rank,
                 int64_t M, int64_t N, int64_t K, void* y, int y_dtype, int flags, void* workspace, size_t ws_bytes,
-                void* stream) {
+                void* stream, bool use_scratch = false) {
   const bool reuse = (flags & NVFP4_GEMM_REUSE_ACT) != 0;
   const bool lora = rank != 0;
-  if ((!a && !reuse) || !w_codes || !w_scales || !w_global || !y || !workspace) return NVFP4_ERR_NULL;
+  if ((!a && !reuse) || !w_codes || !w_scales || !w_global || !y || (!workspace && !use_scratch))
+    return NVFP4_ERR_NULL;
   if (lora && ((!lora_down && !reuse) || !lora_up)) return NVFP4_ERR_NULL;
   if (flags & ~1) return NVFP4_ERR_FLAGS;
   if (y_dtype != NVFP4_F32 && y_dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
@@ -121,14 +156,20 @@ int gemm_common(const void* a, const float* a_global, const uint8_t* w_codes, co
     return NVFP4_ERR_UNSUPPORTED;
   if (lora && (rank % 16 != 0 || rank > kMaxLoraRank)) return NVFP4_ERR_UNSUPPORTED;
   if ((!reuse && !aligned(a, 16)) || !aligned(w_codes, 16) || !aligned(w_scales, 4) || !aligned(w_global, 4) ||
-      (a_global && !aligned(a_global, 4)) || !aligned(y, 16) || !aligned(workspace, 256))
+      (a_global && !aligned(a_global, 4)) || !aligned(y, 16) || (!use_scratch && !aligned(workspace, 256)))
     return NVFP4_ERR_ALIGN;
   if (lora && ((!reuse && !aligned(lora_down, 16)) || !aligned(lora_up, 16))) return NVFP4_ERR_ALIGN;
   if (smooth && !reuse && !aligned(smooth, 16)) return NVFP4_ERR_ALIGN;
-  if (ws_bytes < (lora ? gemm_lora_ws_bytes(M, K) : gemm_ws_bytes(M, K))) return NVFP4_ERR_WORKSPACE;
+  const size_t need = lora ? gemm_lora_ws_bytes(M, K) : gemm_ws_bytes(M, K);
+  if (use_scratch ? need > NVFP4_NOALLOC_SCRATCH_BYTES : ws_bytes < need)
+    return use_scratch ? NVFP4_ERR_SCRATCH : NVFP4_ERR_WORKSPACE;
   if (M == 0 || N == 0) return NVFP4_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (const int st = stream_status(s); st != NVFP4_OK) return st;
+  if (use_scratch) {
+    if (const int st = noalloc_scratch(&workspace); st != NVFP4_OK) return st;
+    ws_bytes = NVFP4_NOALLOC_SCRATCH_BYTES;
+  }
   char* ws = reinterpret_cast<char*>(workspace);
   float* sga = reinterpret_cast<float*>(ws);
   uint16_t* a_hat = reinterpret_cast<uint16_t*>(ws + 256);
@@ -186,6 +227,7 @@ const char* nvfp4_status_string(int status) {
     case NVFP4_ERR_LAUNCH: return "HIP kernel launch failed";
     case NVFP4_ERR_FLAGS: return "unknown flag bits";
     case NVFP4_ERR_CAPTURE: return "the stream is being captured into a HIP graph; calls are not capture-safe";
+    case NVFP4_ERR_SCRATCH: return "the call needs more than the 64 MiB fixed scratch of nvfp4_gemm_w4a4_noalloc";
     default: return "unknown status";
   }
 }
@@ -274,6 +316,13 @@ int nvfp4_gemm_w4a4(const void* a, const float* a_global, const uint8_t* w_codes
                     void* workspace, size_t ws_bytes, void* stream) {
   return gemm_common(a, a_global, w_codes, w_scales, w_global, nullptr, nullptr, nullptr, 0, M, N, K, y, y_dtype,
                      flags, workspace, ws_bytes, stream);
+}
+
+int nvfp4_gemm_w4a4_noalloc(const void* a, const float* a_global, const uint8_t* w_codes, const uint8_t* w_scales,
+                            const float* w_global, int64_t M, int64_t N, int64_t K, void* y, int y_dtype, int flags,
+                            void* stream) {
+  return gemm_common(a, a_global, w_codes, w_scales, w_global, nullptr, nullptr, nullptr, 0, M, N, K, y, y_dtype,
+                     flags, nullptr, 0, stream, true);
 }
 
 int nvfp4_gemm_w4a4_lora(const void* a, const float* a_global, const uint8_t* w_codes, const uint8_t* w_scales,

@@ -13,8 +13,9 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_LAUNCH, ERR_FLAGS, ERR_CAPTURE = (
-    range(10))
+(OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_LAUNCH, ERR_FLAGS, ERR_CAPTURE,
+ ERR_SCRATCH) = range(11)
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 F32, BF16 = 0, 1
 GLOBAL_COMPUTE, GLOBAL_GIVEN = 0, 1
 OP_QUANTIZE, OP_GEMM_W4A4, OP_GEMV_W4A16, OP_GEMM_W4A4_LORA, OP_ACT_CALIBRATE, OP_GEMM_W4A4_SPLITK = (
@@ -31,6 +32,7 @@ SIGNATURES = {
     "nvfp4_dequant": (_I, [_P, _P, _P, _I64, _I64, _P, _I, _P]),
     "nvfp4_gemv_w4a16": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _SZ, _P]),
     "nvfp4_gemm_w4a4": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _I, _P, _SZ, _P]),
+    "nvfp4_gemm_w4a4_noalloc": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _I, _P]),
     "nvfp4_gemm_w4a4_lora": (_I, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I, _I, _P, _SZ, _P]),
     "nvfp4_gemm_w4a4_svdq": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I, _I, _P, _SZ,
                                   _P]),
@@ -258,6 +260,27 @@ def gemm_w4a4(a, w_codes, w_scales, w_global, a_global=None, out_dtype=torch.bfl
                                     _ptr(smooth), _ptr(down), _ptr(up), r, M, N, K, _ptr(out),
                                     _dtype_code(out.dtype), flags, _ptr(ws), ws.numel(), _stream())
     _check("nvfp4_gemm_w4a4_svdq", st)
+    return out
+
+
+def gemm_w4a4_noalloc(a, w_codes, w_scales, w_global, a_global=None, out_dtype=torch.bfloat16, out=None,
+                      reuse_act=False):
+    """The W4A4 product through nvfp4_gemm_w4a4_noalloc: the library's fixed
+    64 MiB per-GPU scratch instead of a workspace (the C call allocates
+    nothing; pass `out` to allocate nothing here either).  reuse_act=True
+    multiplies the activation the previous call of this function on this GPU
+    quantized (same a)."""
+    _need_cuda(a, w_codes, w_scales, w_global, a_global)
+    if a.dtype != torch.bfloat16 or a.dim() != 2:
+        raise ValueError("a must be a 2-D bfloat16 tensor")
+    M, K = a.shape
+    N = _check_weight(w_codes, w_scales, K)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    flags = GEMM_REUSE_ACT if reuse_act else GEMM_QUANTIZE_ACT
+    st = lib().nvfp4_gemm_w4a4_noalloc(_ptr(a), _ptr(a_global), _ptr(w_codes), _ptr(w_scales), _ptr(w_global), M, N,
+                                       K, _ptr(out), _dtype_code(out.dtype), flags, _stream())
+    _check("nvfp4_gemm_w4a4_noalloc", st)
     return out
 
 

@@ -3,7 +3,8 @@
  *   - block quantizers: nvfp4_quantize_absmax, nvfp4_quantize_mse,
  *     nvfp4_quantize_4o6 (four-over-six), and nvfp4_dequant;
  *   - W4A16 decode product: nvfp4_gemv_w4a16;
- *   - W4A4 product with per-call activation quantization: nvfp4_gemm_w4a4,
+ *   - W4A4 product with per-call activation quantization: nvfp4_gemm_w4a4
+ *     (and nvfp4_gemm_w4a4_noalloc, its variant on a fixed device scratch),
  *     with a fused 16-bit low-rank (LoRA) branch: nvfp4_gemm_w4a4_lora, and
  *     on an SVDQuant-smoothed input: nvfp4_gemm_w4a4_svdq;
  *   - calibration of a static activation scale: nvfp4_act_amax,
@@ -75,8 +76,12 @@ typedef enum {
   NVFP4_ERR_UNSUPPORTED = 6, /* valid NVFP4 shape outside the kernels' range (K % 32, M > 16, ...) */
   NVFP4_ERR_LAUNCH = 7,      /* the HIP runtime reported an error at launch */
   NVFP4_ERR_FLAGS = 8,       /* unknown flag bits */
-  NVFP4_ERR_CAPTURE = 9      /* `stream` is being captured into a HIP graph (calls are not capture-safe) */
+  NVFP4_ERR_CAPTURE = 9,     /* `stream` is being captured into a HIP graph (calls are not capture-safe) */
+  NVFP4_ERR_SCRATCH = 10     /* nvfp4_gemm_w4a4_noalloc: the call needs more than its fixed scratch */
 } nvfp4_status;
+
+/* Size of the fixed per-GPU device scratch of nvfp4_gemm_w4a4_noalloc. */
+#define NVFP4_NOALLOC_SCRATCH_BYTES ((size_t)64 * 1024 * 1024)
 
 typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1 } nvfp4_dtype;
 
@@ -223,6 +228,36 @@ int nvfp4_gemm_w4a4(const void* a, const float* a_global, const uint8_t* w_codes
                     const uint8_t* w_scales, const float* w_global,
                     int64_t M, int64_t N, int64_t K, void* y, int y_dtype, int flags,
                     void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * nvfp4_gemm_w4a4_noalloc -- nvfp4_gemm_w4a4 for callers that cannot
+ * allocate device memory (tight serving loops, harnesses that forbid
+ * allocation): the same product, kernels and results, with no workspace
+ * argument.  Its scratch is a fixed array of NVFP4_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) in device memory that the library holds on every GPU it runs on
+ * until the process ends; the call itself allocates and frees nothing.
+ *   a, a_global, w_codes, w_scales, w_global, M, N, K, y, y_dtype: as
+ *            nvfp4_gemm_w4a4
+ *   The call needs nvfp4_workspace_bytes(NVFP4_OP_GEMM_W4A4, M, K) bytes of
+ *   scratch (about 2 M K): larger calls return NVFP4_ERR_SCRATCH before
+ *   anything is launched.  Short activations split K (as nvfp4_gemm_w4a4
+ *   with the split-K extra) when the partial sums fit in the rest of the
+ *   scratch.
+ *   flags    NVFP4_GEMM_QUANTIZE_ACT, or NVFP4_GEMM_REUSE_ACT: the scratch
+ *            still holds the quantized activation of the same [M, K] input
+ *            from the previous call of this function on this GPU
+ *            (several weights sharing one input).
+ * Every call on a GPU uses that GPU's one scratch array and leaves its
+ * contents behind for the next (laid out as nvfp4_gemm_w4a4's workspace;
+ * no part of it has to start at zero: each call writes what it reads).
+ * Calls that may overlap on one GPU (different streams, or host threads
+ * without ordering) race on it; the caller serializes them, e.g. by issuing
+ * them on one stream.
+ */
+int nvfp4_gemm_w4a4_noalloc(const void* a, const float* a_global, const uint8_t* w_codes,
+                            const uint8_t* w_scales, const float* w_global,
+                            int64_t M, int64_t N, int64_t K, void* y, int y_dtype, int flags,
+                            void* stream);
 
 /*
  * nvfp4_gemm_w4a4_lora -- the W4A4 product plus a 16-bit low-rank branch,

@@ -25,15 +25,15 @@ def header_functions():
 def test_library_exports_every_declared_symbol():
     L = nv.lib()
     names = header_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), n
         assert n in nv.SIGNATURES, n
 
 
 def test_status_strings_and_version():
-    assert nv.lib().nvfp4_version() == 10600
-    for s in range(10):
+    assert nv.lib().nvfp4_version() == 10700
+    for s in range(11):
         assert nv.status_string(s) and nv.status_string(s) != "unknown status"
     assert nv.status_string(99) == "unknown status"
 
@@ -203,3 +203,33 @@ def test_python_layer_rejects_mismatched_packed_shapes():
     with pytest.raises(ValueError):
         nv._check_weight(codes, scales, 128)          # codes halved twice, as a BF16-read-as-FP4 mistake
     assert nv._check_weight(codes, scales, 64) == 8
+
+
+def test_gemm_noalloc_validation():
+    """The allocation-free W4A4 entry point checks its arguments like the
+    workspace one, and refuses calls larger than its fixed scratch before
+    any HIP call (the scratch is never looked up on these paths)."""
+    f = nv.lib().nvfp4_gemm_w4a4_noalloc
+
+    def call(a=A16, ag=None, wc=A16, ws=A4, wg=A4, M=64, N=64, K=64, y=A16, ydt=nv.BF16, flags=0):
+        return f(a, ag, wc, ws, wg, M, N, K, y, ydt, flags, None)
+
+    assert call(a=None) == nv.ERR_NULL
+    assert call(a=None, flags=nv.GEMM_REUSE_ACT, M=0) == nv.OK     # reuse: a unused
+    assert call(wc=None) == nv.ERR_NULL
+    assert call(y=None) == nv.ERR_NULL
+    assert call(flags=2) == nv.ERR_FLAGS
+    assert call(ydt=5) == nv.ERR_DTYPE
+    assert call(M=-1) == nv.ERR_SHAPE
+    assert call(K=24) == nv.ERR_SHAPE
+    assert call(K=96) == nv.ERR_UNSUPPORTED
+    assert call(a=A16 + 4) == nv.ERR_ALIGN
+    assert call(M=0) == nv.OK and call(N=0) == nv.OK
+    # the largest activation that fits: workspace bytes <= NVFP4_NOALLOC_SCRATCH_BYTES
+    assert nv.workspace_bytes(nv.OP_GEMM_W4A4, 4096, 4096) <= nv.NOALLOC_SCRATCH_BYTES
+    assert nv.workspace_bytes(nv.OP_GEMM_W4A4, 4096, 12288) > nv.NOALLOC_SCRATCH_BYTES
+    assert call(M=4096, K=12288) == nv.ERR_SCRATCH
+    assert call(M=1 << 20, K=4096) == nv.ERR_SCRATCH
+    assert nv.status_string(nv.ERR_SCRATCH).startswith("the call needs more than")
+    m = re.search(r"#define NVFP4_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) \* 1024 \* 1024\)", open(HEADER).read())
+    assert m and int(m.group(1)) * 1024 * 1024 == nv.NOALLOC_SCRATCH_BYTES
