@@ -43,6 +43,7 @@ HBM_PEAK = 8.0e12           # bytes/s
 MFMA16_PEAK = 2.5e15        # dense fp16/bf16 MFMA flop/s
 VALU_PEAK = 256 * 64 * 2.4e9  # non-packed fp32/fp64 lane-ops/s: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz
 GEMV_COPIES = 16            # 16 x 33 MB = 529 MB, twice the 256 MB MALL (8 copies measured the same)
+DIT_SUSTAINED_BLOCKS = 4    # DiT blocks run back to back in the sustained stage
 
 
 def parse():
@@ -72,6 +73,32 @@ def kernel_source_hash():
         with open(os.path.join(ROOT, "dit_quantization_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+VALU_FILE = os.path.join(ROOT, "profiles", "quantize_mse_valu.json")
+
+
+def mse_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for name in ("quantize_mse.hip", "device_common.hpp"):
+        with open(os.path.join(ROOT, "dit_quantization_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_mse_lane_ops():
+    """VALU lane-operations per element of the MSE search, counted with
+    rocprofv3 (SQ_INSTS_VALU x 64 / elements) on the layer set, or None when
+    the kernel source changed after the counters were taken."""
+    try:
+        with open(VALU_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_hash") != mse_source_hash():
+        return None
+    return d.get("lane_ops_per_element")
 
 
 def stored_traffic():
@@ -155,6 +182,7 @@ def main():
 
     # ------------------------------------------------------------ quantize
     layer_elems = 0
+    mse_ops_source = None
     if "quantize" in phases:
         log("[setup] layer set")
         qbuf = []
@@ -201,7 +229,11 @@ def main():
 
         capture("quantize_absmax_dynamic", q_dynamic, nbytes=n * (4 + 4 + 0.5625))
         capture("quantize_absmax_pass", q_pass, nbytes=n * (4 + 0.5625))
-        capture("quantize_mse", q_mse, nbytes=n * (4 + 0.5625), ops=mse_ops)
+        # ALU work of the MSE search: the counted lane-ops per element when
+        # they were taken on this kernel source, else the op model
+        counted = stored_mse_lane_ops()
+        mse_ops_source = "rocprofv3 SQ_INSTS_VALU" if counted else "model: 6 ops per element and candidate"
+        capture("quantize_mse", q_mse, nbytes=n * (4 + 0.5625), ops=counted * n if counted else mse_ops)
         # four-over-six: at most 2 candidates per block, 16 elements x 6 ops each
         capture("quantize_4o6", q_4o6, nbytes=n * (4 + 0.5625), ops=n / 16 * 2 * 16 * 6.0)
 
@@ -322,6 +354,16 @@ def main():
             dit_phases(dit_img, dit_txt)
 
         capture("gemm_dit_block", dit_block, flops=dit_flops)
+
+        # The linears of consecutive blocks / denoising steps back to back,
+        # with no idle gap between blocks (reported beside the isolated block,
+        # outside value).
+        def dit_blocks_sustained():
+            for _ in range(DIT_SUSTAINED_BLOCKS):
+                dit_phases(dit_img, dit_txt)
+
+        capture("dit_block_sustained", dit_blocks_sustained, flops=DIT_SUSTAINED_BLOCKS * dit_flops,
+                calls=DIT_SUSTAINED_BLOCKS)
 
     if "calibrate" in phases:
         # Static activation scale: running amax + FP8 candidate sweep over
@@ -502,8 +544,10 @@ def main():
     family = {"quantize_mse": "mse", "quantize_4o6": "mse", "quantize_absmax_pass": "absmax",
               "quantize_absmax_dynamic": "absmax"}
     share = {}
+    gemm_family = ("dit_block_sustained", "lora_dit_block", "svdq_dit_block", "static_prefill_gate")
     for k in names:
-        f = family.get(k, "gemm" if k.startswith("gemm_") else "gemv" if k.startswith("gemv_") else k)
+        f = family.get(k, "gemm" if k.startswith("gemm_") or k in gemm_family else "gemv" if k.startswith("gemv_")
+                       else k)
         share[f] = share.get(f, 0.0) + per[k]["us"]
     representative = {"mse": "quantize_mse", "absmax": "quantize_absmax_pass", "gemm": "gemm_prefill_up_reuse"}
     top = max(share, key=share.get)
@@ -534,10 +578,12 @@ def main():
     if roofline is not None:
         ref = None
         if peaks and roofline["bound"] == "mfma":
-            ref = peaks["bf16_gemm_TFLOP_s"]
+            ref = peaks["mfma_f16_loop_TFLOP_s"]
+            roofline["frac_vs_vendor_bf16_gemm"] = roofline["achieved"] / peaks["bf16_gemm_TFLOP_s"]
         elif peaks and roofline["bound"] == "hbm":
-            ref = peaks["hbm_copy_GB_s"]
+            ref = peaks["hbm_read_1GiB_GB_s"]
         roofline["frac_vs_measured"] = roofline["achieved"] / ref if ref else None
+        roofline["measured_peak"] = ref
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(comps)
 
@@ -558,6 +604,7 @@ def main():
         "components": {k: round(v, 5) for k, v in comps.items()},
         "stages": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in per.items()},
         "roofline": roofline,
+        "mse_ops_source": mse_ops_source if "quantize" in phases else None,
         "measured_peaks": peaks,
         "cpu_baseline": cpu,
     }
@@ -565,37 +612,84 @@ def main():
 
 
 def measured_peaks(torch, dev):
-    """Rates this GPU reaches on plain work, next to the datasheet peaks: a
-    1 GiB device-to-device copy (read + write bytes) and a bf16 8192^3 matrix
-    product through torch (the vendor GEMM library)."""
+    """Rates this GPU reaches on plain work, next to the datasheet peaks:
+    - mfma_f16_loop_TFLOP_s: back-to-back v_mfma_f32_32x32x16_f16 with no
+      memory traffic (the probe library), the matrix cores' ceiling at the
+      running clock;
+    - hbm_read_33MB_GB_s: one streaming read of a 33 MB buffer per launch
+      (each workgroup one contiguous segment, the best of three grid sizes),
+      rotating over 16 copies (529 MB, twice the MALL) like the decode GEMV's
+      weights: the read ceiling at the GEMV's size (launch ramp included);
+    - hbm_read_1GiB_GB_s: the same read over 1 GiB (best of two grids);
+    - hbm_copy_GB_s: a 1 GiB device-to-device copy (read + write bytes);
+    - bf16_gemm_TFLOP_s: a bf16 8192^3 product through torch (the vendor
+      GEMM library).
+    Each is the best of several launches timed with HIP events on torch's
+    current stream (the stream the probes launch on)."""
+    import ctypes
     out = {}
+    probes = ctypes.CDLL(os.path.join(ROOT, "dit_quantization_amd", "libnvfp4_probes.so"))
+    probes.probe_mfma_f16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    probes.probe_mfma_f16_flops.restype = ctypes.c_double
+    probes.probe_mfma_f16_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    probes.probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def best_of(fn, reps=5):
+        best = None
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) / 1e3
+            best = t if best is None else min(best, t)
+        return best
+
+    blocks, iters = 256 * 8, 2048
+    mout = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+
+    def mfma():
+        if probes.probe_mfma_f16(ctypes.c_void_p(mout.data_ptr()), blocks, iters, sp) != 0:
+            raise RuntimeError("probe_mfma_f16 launch failed")
+
+    mfma()
+    out["mfma_f16_loop_TFLOP_s"] = probes.probe_mfma_f16_flops(blocks, iters) / best_of(mfma) / 1e12
+    del mout
+    rout = torch.empty(1 << 14, dtype=torch.int32, device=dev)
+    gemv_bytes = 14336 * 4096 * 9 // 16            # 33,030,144 B: one decode weight (codes + scales)
+    copies = [torch.empty(gemv_bytes, dtype=torch.uint8, device=dev) for _ in range(GEMV_COPIES)]
+
+    def reader(bufs, nbytes, blocks):
+        def run():
+            for c in bufs:
+                probes.probe_read(ctypes.c_void_p(c.data_ptr()), nbytes, ctypes.c_void_p(rout.data_ptr()), blocks, sp)
+        return run
+
+    best = 0.0
+    for blocks in (1024, 2048, 4096):              # workgroups of 256 lanes, one contiguous segment each
+        run = reader(copies, gemv_bytes, blocks)
+        run()
+        best = max(best, GEMV_COPIES * gemv_bytes / best_of(run) / 1e9)
+    out["hbm_read_33MB_GB_s"] = best
+    del copies
     n = 1 << 30
     src = torch.empty(n, dtype=torch.uint8, device=dev)
+    best = 0.0
+    for blocks in (2048, 8192):
+        run = reader([src], n, blocks)
+        run()
+        best = max(best, n / best_of(run) / 1e9)
+    out["hbm_read_1GiB_GB_s"] = best
     dst = torch.empty_like(src)
-    best = None
-    for _ in range(5):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        dst.copy_(src)
-        e1.record()
-        torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) / 1e3
-        best = t if best is None else min(best, t)
-    out["hbm_copy_GB_s"] = 2.0 * n / best / 1e9
-    del src, dst
+    out["hbm_copy_GB_s"] = 2.0 * n / best_of(lambda: dst.copy_(src)) / 1e9
+    del src, dst, rout
     a = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
     b = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
     c = a @ b
-    best = None
-    for _ in range(5):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        c = a @ b
-        e1.record()
-        torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) / 1e3
-        best = t if best is None else min(best, t)
-    out["bf16_gemm_TFLOP_s"] = 2.0 * 8192 ** 3 / best / 1e12
+    out["bf16_gemm_TFLOP_s"] = 2.0 * 8192 ** 3 / best_of(lambda: torch.matmul(a, b, out=c)) / 1e12
     del a, b, c
     torch.cuda.synchronize()
     return {k: round(v, 1) for k, v in out.items()}
@@ -614,50 +708,60 @@ def cpu_model():
 
 def cpu_baseline(gpu_comps):
     """The CPU oracle (plain C, fp64, OpenMP over blocks/pairs) on a bounded
-    sample of the same workloads, expressed in the same unit."""
+    sample of the same workloads, expressed in the same unit: once on every
+    core the process may run on, once on one thread."""
     import oracle
     from dit_quantization_amd import inputs
     cores = len(os.sched_getaffinity(0))
-    res = {}
-    # quantize (absmax) on the layer set's q tensor (2^24 elements)
     (_, w), = list(inputs.layerset(["q"]))
-    xs = w
-    t = time.perf_counter()
-    oracle.quantize(xs, oracle.ABSMAX, threads=cores)
-    dt = time.perf_counter() - t
-    qfrac = xs.size * (4 + 4 + 0.5625) / dt / HBM_PEAK
-    res["quantize_GB_s"] = xs.size * (4 + 4 + 0.5625) / dt / 1e9
-    # MSE on 2^20 elements
-    xm = w[:256]
-    t = time.perf_counter()
-    oracle.quantize(xm, oracle.MSE, threads=cores)
-    res["mse_GB_s"] = xm.size * (4 + 0.5625) / (time.perf_counter() - t) / 1e9
-    # GEMV: M = 1 against 4096 rows of the 14336 x 4096 weight
     w1 = inputs.normal_f32((4096, 4096), 1, 0.02)
     c, s, sg = oracle.quantize(w1, threads=cores)
     x = inputs.bf16_bits_to_f32(inputs.gemv_x(4096, 1))
-    t = time.perf_counter()
-    oracle.dot_w4a16(x, c, s, sg, threads=cores)
-    dt = time.perf_counter() - t
-    gbytes = 4096 * 4096 * 0.5625 + 2 * 4096 + 2 * 4096
-    gfrac = gbytes / dt / HBM_PEAK
-    res["gemv_GB_s"] = gbytes / dt / 1e9
-    # W4A4: 128 x 1024 outputs of the prefill product (K = 4096)
     a = inputs.bf16_bits_to_f32(inputs.prefill_activation()[:128])
-    ac, as_, asg = oracle.quantize(a, threads=cores)
-    wc, ws_, wsg = c[:1024], s[:1024], sg
-    t = time.perf_counter()
-    oracle.dot_w4a4(ac, as_, asg, wc, ws_, wsg, 4096, threads=cores)
-    dt = time.perf_counter() - t
-    flops = 2.0 * 128 * 1024 * 4096
-    mfrac = flops / dt / MFMA16_PEAK
-    res["gemm_GFLOP_s"] = flops / dt / 1e9
-    value = 100.0 * (qfrac + gfrac + mfrac) / 3
+
+    def sample(threads):
+        res = {}
+        # quantize (absmax with its amax pass) on the layer set's q tensor (2^24 elements)
+        t = time.perf_counter()
+        oracle.quantize(w, oracle.ABSMAX, threads=threads)
+        dt = time.perf_counter() - t
+        qfrac = w.size * (4 + 4 + 0.5625) / dt / HBM_PEAK
+        res["quantize_GB_s"] = w.size * (4 + 4 + 0.5625) / dt / 1e9
+        # MSE on 2^20 elements
+        xm = w[:256]
+        t = time.perf_counter()
+        oracle.quantize(xm, oracle.MSE, threads=threads)
+        res["mse_GB_s"] = xm.size * (4 + 0.5625) / (time.perf_counter() - t) / 1e9
+        # GEMV: M = 1 against a 4096 x 4096 weight
+        t = time.perf_counter()
+        oracle.dot_w4a16(x, c, s, sg, threads=threads)
+        dt = time.perf_counter() - t
+        gbytes = 4096 * 4096 * 0.5625 + 2 * 4096 + 2 * 4096
+        gfrac = gbytes / dt / HBM_PEAK
+        res["gemv_GB_s"] = gbytes / dt / 1e9
+        # W4A4: 128 x 1024 outputs of the prefill product (K = 4096), activation quantization included
+        t = time.perf_counter()
+        ac, as_, asg = oracle.quantize(a, threads=threads)
+        oracle.dot_w4a4(ac, as_, asg, c[:1024], s[:1024], sg, 4096, threads=threads)
+        dt = time.perf_counter() - t
+        flops = 2.0 * 128 * 1024 * 4096
+        mfrac = flops / dt / MFMA16_PEAK
+        res["gemm_GFLOP_s"] = flops / dt / 1e9
+        return 100.0 * (qfrac + gfrac + mfrac) / 3, {k: round(v, 4) for k, v in res.items()}
+
+    t0 = time.perf_counter()
+    value, comps = sample(cores)
+    t_all = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    value1, comps1 = sample(1)
+    t_one = time.perf_counter() - t0
     return {"value": value, "unit": "% of MI355X peak (same formula as value)", "cores": cores, "kind": "oracle",
             "cpu_model": cpu_model(),
             "sample": "absmax quantize of the 4096x4096 fp32 q tensor (with amax), MSE of 256x4096, "
-                      "W4A16 M=1 x 4096x4096 weight, W4A4 128x1024 outputs of the prefill product (K=4096)",
-            "components": {k: round(v, 4) for k, v in res.items()}}
+                      "W4A16 M=1 x 4096x4096 weight, W4A4 128x1024 outputs of the prefill product (K=4096, "
+                      "activation quantization included)",
+            "components": comps, "sample_seconds": round(t_all, 2),
+            "single_thread": {"value": value1, "cores": 1, "components": comps1, "sample_seconds": round(t_one, 2)}}
 
 
 if __name__ == "__main__":

@@ -12,6 +12,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libnvfp4.so")
+# Reference-rate probes the benchmark measures the chip with (not the NVFP4 path).
+PROBES_SRC = os.path.join(HERE, "probes", "peaks.hip")
+PROBES_OUT = os.path.join(HERE, "libnvfp4_probes.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument"]
@@ -41,7 +44,20 @@ def build(verbose: bool = False, extra=()) -> str:
         os.remove(tmp)
         raise RuntimeError("libnvfp4.so has unresolved library symbols: " + ", ".join(missing or [nm.stderr]))
     os.replace(tmp, OUT)
+    build_probes(verbose)
     return OUT
+
+
+def build_probes(verbose: bool = False) -> str:
+    tmp = PROBES_OUT + ".tmp"
+    cmd = [HIPCC] + FLAGS + [PROBES_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed on the probes:\n" + (r.stderr or ""))
+    os.replace(tmp, PROBES_OUT)
+    return PROBES_OUT
 
 
 if __name__ == "__main__":

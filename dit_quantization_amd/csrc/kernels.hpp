@@ -11,6 +11,22 @@ constexpr int kMaxAmaxPartials = 2048;
 constexpr int kSweepCandidates = 17;  // static activation scale candidates, E4M3 448 down to 112
 
 int amax_partial_count(int64_t n_elems, bool bf16);
+// Per-workgroup partial max |x| of a tensor (amax_partial_count of them),
+// without the finalize pass; the plain and the SVDQuant-smoothed input.
+hipError_t launch_amax_partials_only(const void* x, bool bf16, int64_t n_elems, float* partials, hipStream_t stream);
+hipError_t launch_amax_smooth_partials_only(const uint16_t* x, int64_t rows, int64_t K, const float* mult,
+                                            float* partials, hipStream_t stream);
+// Where an activation-quantization pass takes its tensor scale s_gA from:
+// a given device fp32 (src), or this call's amax partials (partials, np),
+// reduced and turned into fp32(amax / 2688) by every workgroup of the pass.
+// The pass's first workgroup writes the scale to `out` (the workspace's
+// s_gA, read by the product that follows).
+struct ActScale {
+  const float* src;
+  const float* partials;
+  int np;
+  float* out;
+};
 hipError_t launch_global_scale(const void* x, bool bf16, int64_t n_elems, float* partials, float* sg_out,
                                hipStream_t stream);
 hipError_t launch_global_scale_smooth(const uint16_t* x, int64_t rows, int64_t K, const float* mult,
@@ -37,13 +53,13 @@ int gemv_splits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemv_w4a16(const uint16_t* x, const uint8_t* codes, const uint8_t* scales, const float* sg,
                              int64_t M, int64_t N, int64_t K, void* y, bool bf16_out, float* partial,
                              hipStream_t stream);
-hipError_t launch_act_quant_f16(const uint16_t* a, int64_t n_elems, const float* sg, uint16_t* a_hat,
+hipError_t launch_act_quant_f16(const uint16_t* a, int64_t n_elems, ActScale sg, uint16_t* a_hat,
                                 hipStream_t stream);
 // K ranges the fused activation-quantization + LoRA-down pass splits each
 // 16-row tile into; splits > 1 needs fp32 partials of splits * M * rank.
 int lora_splits(int64_t M, int64_t K);
 // mult != nullptr: SVDQuant smoothing, the pass works on bf16(x_k mult_k).
-hipError_t launch_act_quant_lora(const uint16_t* a, const float* sg, const uint16_t* down, int rank, int64_t M,
+hipError_t launch_act_quant_lora(const uint16_t* a, ActScale sg, const uint16_t* down, int rank, int64_t M,
                                  int64_t K, const float* mult, uint16_t* a_hat, uint16_t* lora_l, float* partial,
                                  hipStream_t stream);
 // Split-K of the W4A4 product (short activations): the most K ranges any K

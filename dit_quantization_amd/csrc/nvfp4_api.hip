@@ -180,19 +180,21 @@ int gemm_common(const void* a, const float* a_global, const uint8_t* w_codes, co
   float* partials = reinterpret_cast<float*>(ws + after_l + (lora ? lora_partial_bytes(M, K) : 0));
   clear_error();
   if (!reuse) {
+    // s_gA: the given scale, or this call's amax partials, which the
+    // quantization pass reduces itself (its first workgroup stores s_gA).
     hipError_t e = hipSuccess;
-    if (a_global) {
-      e = hipMemcpyAsync(sga, a_global, sizeof(float), hipMemcpyDeviceToDevice, s);
-    } else if (smooth) {
-      e = launch_global_scale_smooth(reinterpret_cast<const uint16_t*>(a), M, K, smooth, partials, sga, s);
-    } else {
-      e = launch_global_scale(a, true, M * K, partials, sga, s);
+    ActScale sc{a_global, nullptr, 0, sga};
+    if (!a_global) {
+      e = smooth ? launch_amax_smooth_partials_only(reinterpret_cast<const uint16_t*>(a), M, K, smooth, partials, s)
+                 : launch_amax_partials_only(a, true, M * K, partials, s);
+      sc.partials = partials;
+      sc.np = amax_partial_count(M * K, true);
     }
     if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
     const uint16_t* ab = reinterpret_cast<const uint16_t*>(a);
-    e = lora ? launch_act_quant_lora(ab, sga, reinterpret_cast<const uint16_t*>(lora_down), rank, M, K, smooth,
+    e = lora ? launch_act_quant_lora(ab, sc, reinterpret_cast<const uint16_t*>(lora_down), rank, M, K, smooth,
                                      a_hat, lora_l, lora_partial, s)
-             : launch_act_quant_f16(ab, M * K, sga, a_hat, s);
+             : launch_act_quant_f16(ab, M * K, sc, a_hat, s);
     if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
   }
   // Split-K partial sums (plain product on short activations) when the

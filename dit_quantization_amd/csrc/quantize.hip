@@ -13,30 +13,41 @@ namespace nvfp4 {
 
 // ---------------------------------------------------------------- amax
 
-// Each workgroup reduces a grid-strided share of the tensor (16-byte loads)
-// to one partial max |x|.  Plain loads: the quantizing pass that follows
-// reads the same tensor and may still find part of it cached (non-temporal
-// loads here measured 2-4 % slower on the DiT block and the dynamic-scale
-// quantize).
+// max |x| over the 8 bf16 or 4 fp32 values of a 16-byte vector.
+template <bool kBF16>
+__device__ __forceinline__ float absmax16(u32x4 v) {
+  float m = 0.0f;
+  if constexpr (kBF16) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      m = fmaxf(m, fabsf(bf16_bits_to_f32(v[j] & 0xFFFFu)));
+      m = fmaxf(m, fabsf(bf16_bits_to_f32(v[j] >> 16)));
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m = fmaxf(m, fabsf(__uint_as_float(v[j])));
+  }
+  return m;
+}
+
+// Each workgroup reduces a grid-strided share of the tensor (16-byte loads,
+// four in flight per lane) to one partial max |x|.  Plain loads: the
+// quantizing pass that follows reads the same tensor and may still find part
+// of it cached (non-temporal loads here measured 2-4 % slower on the DiT
+// block and the dynamic-scale quantize).
 template <bool kBF16>
 __global__ __launch_bounds__(256) void amax_partial_kernel(const void* __restrict__ x, int64_t n_vec,
                                                            float* __restrict__ partials) {
   float m = 0.0f;
   const u32x4* xv = reinterpret_cast<const u32x4*>(x);
-  int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_vec; i += stride) {
-    u32x4 v = xv[i];
-    if constexpr (kBF16) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        m = fmaxf(m, fabsf(bf16_bits_to_f32(v[j] & 0xFFFFu)));
-        m = fmaxf(m, fabsf(bf16_bits_to_f32(v[j] >> 16)));
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) m = fmaxf(m, fabsf(__uint_as_float(v[j])));
-    }
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n_vec; i += 4 * stride) {
+    const u32x4 v0 = xv[i], v1 = xv[i + stride], v2 = xv[i + 2 * stride], v3 = xv[i + 3 * stride];
+    m = fmaxf(m, fmaxf(fmaxf(absmax16<kBF16>(v0), absmax16<kBF16>(v1)),
+                       fmaxf(absmax16<kBF16>(v2), absmax16<kBF16>(v3))));
   }
+  for (; i < n_vec; i += stride) m = fmaxf(m, absmax16<kBF16>(xv[i]));
   __shared__ float red[4];
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
@@ -47,23 +58,24 @@ __global__ __launch_bounds__(256) void amax_partial_kernel(const void* __restric
 // The same over the SVDQuant-smoothed bf16 activation bf16(x_k m_k) of a
 // row-major [rows, K] tensor (K % 8 == 0): rounding is monotonic, so the
 // largest smoothed magnitude is the smoothed value of the largest |x m|.
+// Two vectors in flight per lane (each also loads its 8 multipliers).
 // Plain loads here too (the SVDQuant DiT block 1.05-1.07 -> 1.04 ms against
 // non-temporal ones).
+__device__ __forceinline__ float absmax_smooth16(u32x4 v, const f32x4* __restrict__ mult, int kv) {
+  return absmax16<true>(smooth8(v, mult[2 * kv], mult[2 * kv + 1]));
+}
+
 __global__ __launch_bounds__(256) void amax_smooth_partial_kernel(const u32x4* __restrict__ x, int64_t n_vec,
                                                                   const f32x4* __restrict__ mult, int kvec,
                                                                   float* __restrict__ partials) {
   float m = 0.0f;
-  int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_vec; i += stride) {
-    const u32x4 v = x[i];
-    const int kv = (int)(i % kvec);
-    const u32x4 h = smooth8(v, mult[2 * kv], mult[2 * kv + 1]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      m = fmaxf(m, fabsf(bf16_bits_to_f32(h[j] & 0xFFFFu)));
-      m = fmaxf(m, fabsf(bf16_bits_to_f32(h[j] >> 16)));
-    }
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + stride < n_vec; i += 2 * stride) {
+    const u32x4 v0 = x[i], v1 = x[i + stride];
+    m = fmaxf(m, fmaxf(absmax_smooth16(v0, mult, (int)(i % kvec)), absmax_smooth16(v1, mult, (int)((i + stride) % kvec))));
   }
+  if (i < n_vec) m = fmaxf(m, absmax_smooth16(x[i], mult, (int)(i % kvec)));
   __shared__ float red[4];
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
@@ -138,7 +150,7 @@ __global__ __launch_bounds__(256) void amax_finalize_kernel(const float* __restr
 
 int amax_partial_count(int64_t n_elems, bool bf16) {
   int64_t n_vec = n_elems / (bf16 ? 8 : 4);
-  int64_t wg = (n_vec + 256 * 8 - 1) / (256 * 8);  // ~8 vectors per thread
+  int64_t wg = (n_vec + 256 * 4 - 1) / (256 * 4);  // ~4 vectors per thread (one batch of loads)
   if (wg < 1) wg = 1;
   if (wg > kMaxAmaxPartials) wg = kMaxAmaxPartials;
   return (int)wg;
@@ -158,6 +170,19 @@ hipError_t launch_global_scale(const void* x, bool bf16, int64_t n_elems, float*
   int np = amax_partial_count(n_elems, bf16);
   launch_amax_partials(x, bf16, n_elems, partials, np, stream);
   hipLaunchKernelGGL(amax_finalize_kernel<false>, dim3(1), dim3(256), 0, stream, partials, np, sg_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax_partials_only(const void* x, bool bf16, int64_t n_elems, float* partials, hipStream_t stream) {
+  launch_amax_partials(x, bf16, n_elems, partials, amax_partial_count(n_elems, bf16), stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax_smooth_partials_only(const uint16_t* x, int64_t rows, int64_t K, const float* mult,
+                                            float* partials, hipStream_t stream) {
+  int np = amax_partial_count(rows * K, true);
+  hipLaunchKernelGGL(amax_smooth_partial_kernel, dim3(np), dim3(256), 0, stream, reinterpret_cast<const u32x4*>(x),
+                     rows * K / 8, reinterpret_cast<const f32x4*>(mult), (int)(K / 8), partials);
   return hipGetLastError();
 }
 

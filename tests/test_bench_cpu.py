@@ -28,3 +28,13 @@ def test_stored_traffic_matches_the_current_kernel_source():
     M, N, K = d["shape"]
     algorithmic = M * K * 2 + N * K * 0.5625 + 2 * M * N
     assert d["hbm_bytes_per_launch"] >= algorithmic   # the counters cannot see less than the compulsory traffic
+
+
+def test_stored_mse_lane_ops_match_the_current_kernel_source():
+    """The committed VALU counter summary of the MSE search was taken on the
+    kernel source as it stands (otherwise bench.py falls back to its op
+    model and says so)."""
+    with open(os.path.join(ROOT, "profiles", "quantize_mse_valu.json")) as f:
+        d = json.load(f)
+    assert d["source_hash"] == bench.mse_source_hash()
+    assert bench.stored_mse_lane_ops() == d["lane_ops_per_element"] > 16 * 6 / 16
