@@ -19,13 +19,13 @@
 // about two thirds of a call; the decode with its per-element block-scale
 // multiply and, at M > 4, the x loads take the rest, so the x operand is
 // built from as few load instructions as possible:
-//  * M <= 4 (staggered): lane (4 j + i, g) loads the 8 values of x[i] that
+//  * M <= 4 on weights of fewer than 8192 rows (staggered): lane (4 j + i, g) loads the 8 values of x[i] that
 //    meet MFMA j in lane group g -- one 16-byte load per lane covers all 4
 //    MFMAs of a super-chunk.  MFMA j keeps only the lanes with j' == j, so
 //    output row 4 j + i collects x[i] times the codes of MFMA j, and the
 //    4 row blocks are added across lane groups at the end.
-//  * M > 4 (dense): lane (m, g) holds x[m] on its lane group's k slots for
-//    each MFMA; 4 loads per super-chunk cover 16 rows.
+//  * otherwise (dense): lane (m, g) holds x[m] on its lane group's k slots for
+//    each MFMA; 4 loads per super-chunk cover 16 rows (rows past M read zeros).
 // Rows past N, chunks past K and x rows past M are buffer loads at an
 // out-of-range offset, which return zero without a memory access.  With the
 // dense layout each 16-row tile is computed as soon as its own DMA has
@@ -480,12 +480,14 @@ hipError_t launch_gemv_w4a16(const uint16_t* x, const uint8_t* codes, const uint
 #undef NVFP4_GEMV_M1
     return hipGetLastError();
   }
-  // M > 1: MFMA kernels.  On weights of at least 8192 rows, 32 rows per
-  // workgroup of 4 waves (M <= 4) or 64 rows of 8 waves (M > 4: each x
-  // fragment then feeds 4 row tiles, and x is read from L2 once per
-  // workgroup); else 16 rows, with 16 waves splitting rows of K >= 8192
-  // (unless the split-K path above took the call).  Chosen by sweeping rows
-  // x waves on the 14336 x 4096 and 4096 x 14336 decode shapes.
+  // M > 1: MFMA kernels.  On weights of at least 8192 rows, the dense layout
+  // with 64 rows per workgroup of 8 waves for every M (each x fragment feeds
+  // 4 row tiles, and x is read from L2 once per workgroup); else 16 rows,
+  // with the staggered layout and 8 waves at M <= 4, and the dense layout
+  // with 16 waves splitting rows of K >= 8192 at M > 4 (unless the split-K
+  // path above took the call).  Chosen by sweeping layout x rows x waves on
+  // the 14336 x 4096 and 4096 x 14336 decode shapes (M = 4: 10.7 -> 10.2 and
+  // 12.0 -> 11.7 us per call against 32-row staggered tiles and 16 waves).
   const int dense = M > 4 ? 1 : 0;
   const bool t2 = N >= 32 * 256;
   const bool nw16 = !t2 && K >= 8192;
@@ -502,15 +504,10 @@ hipError_t launch_gemv_w4a16(const uint16_t* x, const uint8_t* codes, const uint
                        splits, n, sg, y, b);
     return hipGetLastError();
   }
-  if (dense) {
-    if (t2) NVFP4_GEMV_MFMA(1, 4, 8);
-    else if (nw16) NVFP4_GEMV_MFMA(1, 1, 16);
-    else NVFP4_GEMV_MFMA(1, 1, 8);
-  } else {
-    if (t2) NVFP4_GEMV_MFMA(0, 2, 4);
-    else if (nw16) NVFP4_GEMV_MFMA(0, 1, 16);
-    else NVFP4_GEMV_MFMA(0, 1, 8);
-  }
+  if (t2) NVFP4_GEMV_MFMA(1, 4, 8);
+  else if (!dense) NVFP4_GEMV_MFMA(0, 1, 8);
+  else if (nw16) NVFP4_GEMV_MFMA(1, 1, 16);
+  else NVFP4_GEMV_MFMA(1, 1, 8);
 #undef NVFP4_GEMV_MFMA
   return hipGetLastError();
 }

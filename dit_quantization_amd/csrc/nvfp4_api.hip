@@ -41,14 +41,18 @@ void clear_error() { (void)hipGetLastError(); }
 int launch_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH; }
 
 // Device address of `scratch` on the current device, looked up once per
-// device (with that device current) and kept.
+// device (with that device current) and kept.  The stream must belong to the
+// current device: the address is that device's copy.
 constexpr int kMaxDevices = 64;
 std::atomic<void*> g_scratch[kMaxDevices];
 std::mutex g_scratch_mu;
 
-int noalloc_scratch(void** out) {
+int noalloc_scratch(hipStream_t stream, void** out) {
   int dev = -1;
+  hipDevice_t sdev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return NVFP4_ERR_LAUNCH;
+  if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return NVFP4_ERR_LAUNCH;
+  if (sdev != dev) return NVFP4_ERR_UNSUPPORTED;
   void* p = g_scratch[dev].load(std::memory_order_acquire);
   if (!p) {
     std::lock_guard<std::mutex> lock(g_scratch_mu);
@@ -167,7 +171,7 @@ int gemm_common(const void* a, const float* a_global, const uint8_t* w_codes, co
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (const int st = stream_status(s); st != NVFP4_OK) return st;
   if (use_scratch) {
-    if (const int st = noalloc_scratch(&workspace); st != NVFP4_OK) return st;
+    if (const int st = noalloc_scratch(s, &workspace); st != NVFP4_OK) return st;
     ws_bytes = NVFP4_NOALLOC_SCRATCH_BYTES;
   }
   char* ws = reinterpret_cast<char*>(workspace);

@@ -252,7 +252,8 @@ int nvfp4_gemm_w4a4(const void* a, const float* a_global, const uint8_t* w_codes
  * no part of it has to start at zero: each call writes what it reads).
  * Calls that may overlap on one GPU (different streams, or host threads
  * without ordering) race on it; the caller serializes them, e.g. by issuing
- * them on one stream.
+ * them on one stream.  `stream` must belong to the current device (the
+ * scratch used is that device's): otherwise NVFP4_ERR_UNSUPPORTED.
  */
 int nvfp4_gemm_w4a4_noalloc(const void* a, const float* a_global, const uint8_t* w_codes,
                             const uint8_t* w_scales, const float* w_global,

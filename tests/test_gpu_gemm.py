@@ -45,9 +45,12 @@ def test_tiny_config_gemv():
     assert_within_tau(y32.reshape(-1), ystar, tau, "tiny fp32")
 
 
-@pytest.mark.parametrize("shape", [(64, 32), (100, 160), (300, 96), (1000, 1056), (33, 4096)])
+@pytest.mark.parametrize("shape", [(64, 32), (100, 160), (300, 96), (1000, 1056), (33, 4096), (8200, 288)])
 @pytest.mark.parametrize("M", [1, 3, 4, 5, 8, 16])
 def test_gemv_ragged(shape, M):
+    """Every M against the oracle on ragged shapes; 8200 rows take the
+    tall-weight kernels (64-row tiles, dense layout also at M <= 4) with a
+    partial last tile."""
     N, K = shape
     print(f"[case] gemv N={N} K={K} M={M}", flush=True)
     w = inputs.student_t_f32((N, K), N + K)
