@@ -365,6 +365,26 @@ def main():
         capture("dit_block_sustained", dit_blocks_sustained, flops=DIT_SUSTAINED_BLOCKS * dit_flops,
                 calls=DIT_SUSTAINED_BLOCKS)
 
+        # The same block with each phase's image and text products in one
+        # grouped launch (nvfp4_gemm_w4a4_group) on one stream: q/k/v of
+        # both streams (6 products), MLP up (2), MLP down (2).
+        def group_phase(names, act):
+            prods = []
+            for ad, hd, w, ws_a, ws_h, outs in dit_calls:
+                a_t, ws_t = (hd, ws_h) if act == "h" else (ad, ws_a)
+                for j, name in enumerate(names):
+                    prods.append({"a": a_t, "w": w[name], "workspace": ws_t, "out": outs[name], "reuse_act": j > 0})
+            return prods
+
+        grouped = [group_phase(["to_q", "to_k", "to_v"], "a"), group_phase(["mlp_up"], "a"),
+                   group_phase(["mlp_down"], "h")]
+
+        def dit_block_grouped():
+            for prods in grouped:
+                nv.gemm_w4a4_group(prods)
+
+        capture("dit_block_grouped", dit_block_grouped, flops=dit_flops)
+
     if "calibrate" in phases:
         # Static activation scale: running amax + FP8 candidate sweep over
         # calibration batches (four 512x3072 text-stream batches and the
@@ -544,7 +564,8 @@ def main():
     family = {"quantize_mse": "mse", "quantize_4o6": "mse", "quantize_absmax_pass": "absmax",
               "quantize_absmax_dynamic": "absmax"}
     share = {}
-    gemm_family = ("dit_block_sustained", "lora_dit_block", "svdq_dit_block", "static_prefill_gate")
+    gemm_family = ("dit_block_sustained", "dit_block_grouped", "lora_dit_block", "svdq_dit_block",
+                   "static_prefill_gate")
     for k in names:
         f = family.get(k, "gemm" if k.startswith("gemm_") or k in gemm_family else "gemv" if k.startswith("gemv_")
                        else k)

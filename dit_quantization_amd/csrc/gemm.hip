@@ -85,12 +85,16 @@ __device__ __forceinline__ f16x2 e4m3x2_to_f16x2(uint32_t b) {
 // partial [splits, M, N]; gemm_splitk_reduce_kernel finishes the product.
 // (A separate instantiation: folding the range offsets into the unsplit
 // kernel cost it 3-5 % on the prefill and DiT shapes.)
+//
+// The body below computes tile `bid` (K range `split` of `splits`) of one
+// product; gemm_w4a4_kernel maps workgroups of one product onto it,
+// gemm_w4a4_group_kernel workgroups of several products (one launch).
 template <int BM, int BN, int WM, int WN, bool LORA, bool SPLIT>
-__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu((BM / WM) * (BN / WN) >= 128 * 128 ? 1 : 2))) void gemm_w4a4_kernel(
-    const uint16_t* __restrict__ a_hat, const float* __restrict__ sga_ptr, const uint8_t* __restrict__ codes,
-    const uint8_t* __restrict__ scales, const float* __restrict__ sgw_ptr, int M, int N, int K, void* __restrict__ y,
-    int bf16_out, const uint16_t* __restrict__ lora_l, const uint16_t* __restrict__ lora_up, int rank, int splits,
-    float* __restrict__ partial) {
+__device__ __forceinline__ void gemm_w4a4_tile(
+    int bid, int split, const uint16_t* __restrict__ a_hat, const float* __restrict__ sga_ptr,
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, const float* __restrict__ sgw_ptr, int M,
+    int N, int K, void* __restrict__ y, int bf16_out, const uint16_t* __restrict__ lora_l,
+    const uint16_t* __restrict__ lora_up, int rank, int splits, float* __restrict__ partial) {
   constexpr int NT = WM * WN * 64;                       // threads
   constexpr int TM = BM / WM / 32, TN = BN / WN / 32;    // 32x32 tiles per wave
   constexpr int A_CHUNKS = BM * BK * 2 / 16;             // 16-byte chunks per A stage
@@ -110,17 +114,8 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu((B
   Stage& st1 = stages[1];
   Stage& st2 = stages[2];
 
-  // Tile coordinates.  Consecutive workgroup ids go to different XCDs
-  // (round robin over 8); remap so each XCD receives a contiguous run of
-  // tiles, which then share A rows / W rows in that XCD's L2.
+  // Tile coordinates (bid already remapped by the caller, see below).
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const int ntiles = tiles_m * tiles_n;
-  const int split = SPLIT ? (int)(blockIdx.x % splits) : 0;
-  int bid = SPLIT ? (int)(blockIdx.x / splits) : (int)blockIdx.x;
-  if (!SPLIT && (ntiles & 7) == 0) {  // a bijection on [0, ntiles) when 8 divides it
-    const int per_xcd = ntiles >> 3;
-    bid = (bid & 7) * per_xcd + (bid >> 3);
-  }
   // Walk tiles in groups of 4 M-tiles so the tiles an XCD runs together
   // share A row panels and W column panels in its L2 (measured on the
   // prefill shape: 401 MB fetched past L2 per launch with groups of 4,
@@ -406,6 +401,48 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu((B
   }
 }
 
+// Consecutive workgroup ids go to different XCDs (round robin over 8);
+// remap so each XCD receives a contiguous run of tiles, which then share A
+// rows / W rows in that XCD's L2 (a bijection on [0, ntiles) when 8
+// divides ntiles).
+__device__ __forceinline__ int xcd_contiguous(int bid, int ntiles) {
+  if ((ntiles & 7) != 0) return bid;
+  return (bid & 7) * (ntiles >> 3) + (bid >> 3);
+}
+
+template <int BM, int BN, int WM, int WN, bool LORA, bool SPLIT>
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu((BM / WM) * (BN / WN) >= 128 * 128 ? 1 : 2))) void gemm_w4a4_kernel(
+    const uint16_t* __restrict__ a_hat, const float* __restrict__ sga_ptr, const uint8_t* __restrict__ codes,
+    const uint8_t* __restrict__ scales, const float* __restrict__ sgw_ptr, int M, int N, int K, void* __restrict__ y,
+    int bf16_out, const uint16_t* __restrict__ lora_l, const uint16_t* __restrict__ lora_up, int rank, int splits,
+    float* __restrict__ partial) {
+  const int ntiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int split = SPLIT ? (int)(blockIdx.x % splits) : 0;
+  const int bid = SPLIT ? (int)(blockIdx.x / splits) : xcd_contiguous((int)blockIdx.x, ntiles);
+  gemm_w4a4_tile<BM, BN, WM, WN, LORA, SPLIT>(bid, split, a_hat, sga_ptr, codes, scales, sgw_ptr, M, N, K, y,
+                                              bf16_out, lora_l, lora_up, rank, splits, partial);
+}
+
+// Several independent products in one launch, each on 256 x 256 tiles
+// ("NVFP4 en difusion ...", section 1: a double-stream DiT block runs the
+// image and the text tokens through separate weights, so each layer is one
+// product per stream).  The products' tiles are numbered end to end and
+// remapped to XCDs as one range; a workgroup finds its product by the
+// table's prefix of tile counts.  Filling one grid with every product of a
+// phase keeps all CUs busy where a single product's last round would not.
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2))) void gemm_w4a4_group_kernel(
+    const GemmGroup g, int bf16_out) {
+  const int total = g.tile_begin[g.n];
+  const int bid = xcd_contiguous((int)blockIdx.x, total);
+  int p = 0;
+#pragma unroll
+  for (int t = 1; t < kMaxGemmGroup; ++t) p += (t < g.n && bid >= g.tile_begin[t]) ? 1 : 0;
+  gemm_w4a4_tile<BM, BN, WM, WN, false, false>(bid - g.tile_begin[p], 0, g.a_hat[p], g.sga[p], g.codes[p],
+                                               g.scales[p], g.sgw[p], g.M[p], g.N[p], g.K[p], g.y[p], bf16_out,
+                                               nullptr, nullptr, 0, 1, nullptr);
+}
+
 // y = round(fp32(s_gA s_gW) * (((p_0 + p_1) + ...) + p_{S-1})) per element.
 __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(const float* __restrict__ partial, int splits,
                                                                  int64_t n, const float* __restrict__ sga_ptr,
@@ -445,6 +482,16 @@ int gemm_splits(int64_t M, int64_t N, int64_t K) {
   const int64_t kts = (kt + s - 1) / s;
   return (int)((kt + kts - 1) / kts);  // no empty range
 }
+
+hipError_t launch_gemm_w4a4_group(const GemmGroup& g, bool bf16_out, hipStream_t stream) {
+  const int total = g.tile_begin[g.n];
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_w4a4_group_kernel<256, 256, 2, 4>), dim3((unsigned)total), dim3(512), 0, stream, g,
+                     bf16_out ? 1 : 0);
+  return hipGetLastError();
+}
+
+int64_t gemm_group_tiles(int64_t M, int64_t N) { return tiles256(M, N); }
 
 hipError_t launch_gemm_w4a4(const uint16_t* a_hat, const float* sga, const uint8_t* codes, const uint8_t* scales,
                             const float* sgw, int64_t M, int64_t N, int64_t K, void* y, bool bf16_out,

@@ -66,6 +66,24 @@ hipError_t launch_act_quant_lora(const uint16_t* a, ActScale sg, const uint16_t*
 // can get for an M x N output, and the count used for a given K.
 int gemm_max_splits(int64_t M, int64_t N);
 int gemm_splits(int64_t M, int64_t N, int64_t K);
+// Several W4A4 products in one launch (256 x 256 tiles, no split, no
+// low-rank branch): the activations are already quantized in each
+// product's workspace.  tile_begin[i] is the first tile of product i
+// (gemm_group_tiles(M, N) tiles each); tile_begin[n] the total.
+constexpr int kMaxGemmGroup = 8;
+struct GemmGroup {
+  int n;
+  int tile_begin[kMaxGemmGroup + 1];
+  const uint16_t* a_hat[kMaxGemmGroup];
+  const float* sga[kMaxGemmGroup];
+  const uint8_t* codes[kMaxGemmGroup];
+  const uint8_t* scales[kMaxGemmGroup];
+  const float* sgw[kMaxGemmGroup];
+  void* y[kMaxGemmGroup];
+  int M[kMaxGemmGroup], N[kMaxGemmGroup], K[kMaxGemmGroup];
+};
+int64_t gemm_group_tiles(int64_t M, int64_t N);
+hipError_t launch_gemm_w4a4_group(const GemmGroup& g, bool bf16_out, hipStream_t stream);
 // partial: fp32 [gemm_splits(M, N, K), M, N] scratch, or nullptr (no split).
 hipError_t launch_gemm_w4a4(const uint16_t* a_hat, const float* sga, const uint8_t* codes, const uint8_t* scales,
                             const float* sgw, int64_t M, int64_t N, int64_t K, void* y, bool bf16_out,

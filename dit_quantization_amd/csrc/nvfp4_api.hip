@@ -21,7 +21,7 @@ namespace {
 
 using namespace nvfp4;
 
-constexpr int kVersion = 1 * 10000 + 7 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 8 * 100 + 0;
 static_assert(kSweepCandidates == NVFP4_SWEEP_CANDIDATES, "candidate count of the activation scale sweep");
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -138,12 +138,13 @@ size_t calibrate_ws_bytes(int64_t n) {
   return amax > sweep ? amax : sweep;
 }
 
-// use_scratch: the allocation-free variant; `workspace` and `ws_bytes` are
-// ignored and the call runs on the fixed per-device scratch.
-int gemm_common(const void* a, const float* a_global, const uint8_t* w_codes, const uint8_t* w_scales,
-                const float* w_global, const float* smooth, const void* lora_down, const void* lora_up, int rank,
-                int64_t M, int64_t N, int64_t K, void* y, int y_dtype, int flags, void* workspace, size_t ws_bytes,
-                void* stream, bool use_scratch = false) {
+// Argument checks of every W4A4 entry point (before any HIP call).
+// use_scratch: the allocation-free variant, whose `workspace` and
+// `ws_bytes` are not the caller's.
+int gemm_check(const void* a, const float* a_global, const uint8_t* w_codes, const uint8_t* w_scales,
+               const float* w_global, const float* smooth, const void* lora_down, const void* lora_up, int rank,
+               int64_t M, int64_t N, int64_t K, const void* y, int y_dtype, int flags, const void* workspace,
+               size_t ws_bytes, bool use_scratch) {
   const bool reuse = (flags & NVFP4_GEMM_REUSE_ACT) != 0;
   const bool lora = rank != 0;
   if ((!a && !reuse) || !w_codes || !w_scales || !w_global || !y || (!workspace && !use_scratch))
@@ -167,40 +168,68 @@ int gemm_common(const void* a, const float* a_global, const uint8_t* w_codes, co
   const size_t need = lora ? gemm_lora_ws_bytes(M, K) : gemm_ws_bytes(M, K);
   if (use_scratch ? need > NVFP4_NOALLOC_SCRATCH_BYTES : ws_bytes < need)
     return use_scratch ? NVFP4_ERR_SCRATCH : NVFP4_ERR_WORKSPACE;
+  return NVFP4_OK;
+}
+
+// Workspace regions of a W4A4 call (layout documented in include/nvfp4.h).
+struct GemmWorkspace {
+  float* sga;
+  uint16_t* a_hat;
+  uint16_t* lora_l;
+  float* lora_partial;
+  float* partials;
+};
+
+GemmWorkspace gemm_workspace(void* workspace, int64_t M, int64_t K, bool lora) {
+  char* ws = reinterpret_cast<char*>(workspace);
+  const size_t after_a = 256 + round256((size_t)M * K * 2);
+  const size_t after_l = after_a + (lora ? round256((size_t)M * kMaxLoraRank * 2) : 0);
+  return {reinterpret_cast<float*>(ws), reinterpret_cast<uint16_t*>(ws + 256), reinterpret_cast<uint16_t*>(ws + after_a),
+          reinterpret_cast<float*>(ws + after_l),
+          reinterpret_cast<float*>(ws + after_l + (lora ? lora_partial_bytes(M, K) : 0))};
+}
+
+// Per-call activation quantization into the workspace: s_gA is the given
+// scale, or this call's amax partials, which the quantization pass reduces
+// itself (its first workgroup stores s_gA).
+hipError_t quantize_activation(const void* a, const float* a_global, const float* smooth, const void* lora_down,
+                               int rank, int64_t M, int64_t K, const GemmWorkspace& w, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  ActScale sc{a_global, nullptr, 0, w.sga};
+  if (!a_global) {
+    e = smooth ? launch_amax_smooth_partials_only(reinterpret_cast<const uint16_t*>(a), M, K, smooth, w.partials, s)
+               : launch_amax_partials_only(a, true, M * K, w.partials, s);
+    sc.partials = w.partials;
+    sc.np = amax_partial_count(M * K, true);
+  }
+  if (e != hipSuccess) return e;
+  const uint16_t* ab = reinterpret_cast<const uint16_t*>(a);
+  return rank ? launch_act_quant_lora(ab, sc, reinterpret_cast<const uint16_t*>(lora_down), rank, M, K, smooth,
+                                      w.a_hat, w.lora_l, w.lora_partial, s)
+              : launch_act_quant_f16(ab, M * K, sc, w.a_hat, s);
+}
+
+int gemm_common(const void* a, const float* a_global, const uint8_t* w_codes, const uint8_t* w_scales,
+                const float* w_global, const float* smooth, const void* lora_down, const void* lora_up, int rank,
+                int64_t M, int64_t N, int64_t K, void* y, int y_dtype, int flags, void* workspace, size_t ws_bytes,
+                void* stream, bool use_scratch = false) {
+  if (const int st = gemm_check(a, a_global, w_codes, w_scales, w_global, smooth, lora_down, lora_up, rank, M, N, K,
+                                y, y_dtype, flags, workspace, ws_bytes, use_scratch);
+      st != NVFP4_OK)
+    return st;
   if (M == 0 || N == 0) return NVFP4_OK;
+  const bool reuse = (flags & NVFP4_GEMM_REUSE_ACT) != 0;
+  const bool lora = rank != 0;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (const int st = stream_status(s); st != NVFP4_OK) return st;
   if (use_scratch) {
     if (const int st = noalloc_scratch(s, &workspace); st != NVFP4_OK) return st;
     ws_bytes = NVFP4_NOALLOC_SCRATCH_BYTES;
   }
-  char* ws = reinterpret_cast<char*>(workspace);
-  float* sga = reinterpret_cast<float*>(ws);
-  uint16_t* a_hat = reinterpret_cast<uint16_t*>(ws + 256);
-  const size_t after_a = 256 + round256((size_t)M * K * 2);
-  uint16_t* lora_l = reinterpret_cast<uint16_t*>(ws + after_a);
-  const size_t after_l = after_a + (lora ? round256((size_t)M * kMaxLoraRank * 2) : 0);
-  float* lora_partial = reinterpret_cast<float*>(ws + after_l);
-  float* partials = reinterpret_cast<float*>(ws + after_l + (lora ? lora_partial_bytes(M, K) : 0));
+  const GemmWorkspace w = gemm_workspace(workspace, M, K, lora);
   clear_error();
-  if (!reuse) {
-    // s_gA: the given scale, or this call's amax partials, which the
-    // quantization pass reduces itself (its first workgroup stores s_gA).
-    hipError_t e = hipSuccess;
-    ActScale sc{a_global, nullptr, 0, sga};
-    if (!a_global) {
-      e = smooth ? launch_amax_smooth_partials_only(reinterpret_cast<const uint16_t*>(a), M, K, smooth, partials, s)
-                 : launch_amax_partials_only(a, true, M * K, partials, s);
-      sc.partials = partials;
-      sc.np = amax_partial_count(M * K, true);
-    }
-    if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
-    const uint16_t* ab = reinterpret_cast<const uint16_t*>(a);
-    e = lora ? launch_act_quant_lora(ab, sc, reinterpret_cast<const uint16_t*>(lora_down), rank, M, K, smooth,
-                                     a_hat, lora_l, lora_partial, s)
-             : launch_act_quant_f16(ab, M * K, sc, a_hat, s);
-    if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
-  }
+  if (!reuse && quantize_activation(a, a_global, smooth, lora_down, rank, M, K, w, s) != hipSuccess)
+    return NVFP4_ERR_LAUNCH;
   // Split-K partial sums (plain product on short activations) when the
   // workspace extends past the regions above by their size.
   float* split_partial = nullptr;
@@ -208,10 +237,10 @@ int gemm_common(const void* a, const float* a_global, const uint8_t* w_codes, co
     const int splits = gemm_splits(M, N, K);
     const size_t base = gemm_ws_bytes(M, K);
     if (splits > 1 && ws_bytes >= base + (size_t)splits * M * N * 4)
-      split_partial = reinterpret_cast<float*>(ws + base);
+      split_partial = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + base);
   }
-  return launch_status(launch_gemm_w4a4(a_hat, sga, w_codes, w_scales, w_global, M, N, K, y,
-                                        y_dtype == NVFP4_BF16, lora ? lora_l : nullptr,
+  return launch_status(launch_gemm_w4a4(w.a_hat, w.sga, w_codes, w_scales, w_global, M, N, K, y,
+                                        y_dtype == NVFP4_BF16, lora ? w.lora_l : nullptr,
                                         reinterpret_cast<const uint16_t*>(lora_up), rank, split_partial, s));
 }
 
@@ -322,6 +351,60 @@ int nvfp4_gemm_w4a4(const void* a, const float* a_global, const uint8_t* w_codes
                     void* workspace, size_t ws_bytes, void* stream) {
   return gemm_common(a, a_global, w_codes, w_scales, w_global, nullptr, nullptr, nullptr, 0, M, N, K, y, y_dtype,
                      flags, workspace, ws_bytes, stream);
+}
+
+int nvfp4_gemm_w4a4_group(const nvfp4_gemm_w4a4_product* products, int64_t n, int y_dtype, void* stream) {
+  if (n < 0) return NVFP4_ERR_SHAPE;
+  if (n > 0 && !products) return NVFP4_ERR_NULL;
+  if (y_dtype != NVFP4_F32 && y_dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
+  for (int64_t i = 0; i < n; ++i) {
+    const nvfp4_gemm_w4a4_product& p = products[i];
+    const int st = gemm_check(p.a, p.a_global, p.w_codes, p.w_scales, p.w_global, nullptr, nullptr, nullptr, 0, p.M,
+                              p.N, p.K, p.y, y_dtype, p.flags, p.workspace, p.ws_bytes, false);
+    if (st != NVFP4_OK) return st;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  bool any = false;
+  for (int64_t i = 0; i < n; ++i) any = any || (products[i].M > 0 && products[i].N > 0);
+  if (!any) return NVFP4_OK;
+  if (const int st = stream_status(s); st != NVFP4_OK) return st;
+  clear_error();
+  // every activation first (in product order), then the products
+  for (int64_t i = 0; i < n; ++i) {
+    const nvfp4_gemm_w4a4_product& p = products[i];
+    if (p.M == 0 || p.N == 0 || (p.flags & NVFP4_GEMM_REUSE_ACT)) continue;
+    if (quantize_activation(p.a, p.a_global, nullptr, nullptr, 0, p.M, p.K,
+                            gemm_workspace(p.workspace, p.M, p.K, false), s) != hipSuccess)
+      return NVFP4_ERR_LAUNCH;
+  }
+  GemmGroup g{};
+  auto flush = [&]() -> hipError_t {
+    const hipError_t e = g.n ? launch_gemm_w4a4_group(g, y_dtype == NVFP4_BF16, s) : hipSuccess;
+    g = GemmGroup{};
+    return e;
+  };
+  for (int64_t i = 0; i < n; ++i) {
+    const nvfp4_gemm_w4a4_product& p = products[i];
+    if (p.M == 0 || p.N == 0) continue;
+    const int64_t tiles = gemm_group_tiles(p.M, p.N);
+    if (tiles > INT32_MAX) return NVFP4_ERR_UNSUPPORTED;  // more tiles than one grid holds
+    if (g.n == kMaxGemmGroup || (int64_t)g.tile_begin[g.n] + tiles > INT32_MAX) {
+      if (flush() != hipSuccess) return NVFP4_ERR_LAUNCH;
+    }
+    const GemmWorkspace w = gemm_workspace(p.workspace, p.M, p.K, false);
+    const int k = g.n++;
+    g.a_hat[k] = w.a_hat;
+    g.sga[k] = w.sga;
+    g.codes[k] = p.w_codes;
+    g.scales[k] = p.w_scales;
+    g.sgw[k] = p.w_global;
+    g.y[k] = p.y;
+    g.M[k] = (int)p.M;
+    g.N[k] = (int)p.N;
+    g.K[k] = (int)p.K;
+    g.tile_begin[k + 1] = g.tile_begin[k] + (int)tiles;
+  }
+  return launch_status(flush());
 }
 
 int nvfp4_gemm_w4a4_noalloc(const void* a, const float* a_global, const uint8_t* w_codes, const uint8_t* w_scales,

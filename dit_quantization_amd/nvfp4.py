@@ -33,6 +33,7 @@ SIGNATURES = {
     "nvfp4_gemv_w4a16": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _P, _SZ, _P]),
     "nvfp4_gemm_w4a4": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _I, _P, _SZ, _P]),
     "nvfp4_gemm_w4a4_noalloc": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I, _I, _P]),
+    "nvfp4_gemm_w4a4_group": (_I, [_P, _I64, _I, _P]),
     "nvfp4_gemm_w4a4_lora": (_I, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I, _I, _P, _SZ, _P]),
     "nvfp4_gemm_w4a4_svdq": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I, _I, _P, _SZ,
                                   _P]),
@@ -45,6 +46,12 @@ SIGNATURES = {
 }
 
 _lib = None
+
+
+class GemmProduct(ctypes.Structure):
+    """nvfp4_gemm_w4a4_product of include/nvfp4.h."""
+    _fields_ = [("a", _P), ("a_global", _P), ("w_codes", _P), ("w_scales", _P), ("w_global", _P), ("M", _I64),
+                ("N", _I64), ("K", _I64), ("y", _P), ("flags", _I), ("workspace", _P), ("ws_bytes", _SZ)]
 
 
 class NVFP4Error(RuntimeError):
@@ -261,6 +268,38 @@ def gemm_w4a4(a, w_codes, w_scales, w_global, a_global=None, out_dtype=torch.bfl
                                     _dtype_code(out.dtype), flags, _ptr(ws), ws.numel(), _stream())
     _check("nvfp4_gemm_w4a4_svdq", st)
     return out
+
+
+def gemm_w4a4_group(products, out_dtype=torch.bfloat16):
+    """Several W4A4 products in one launch (nvfp4_gemm_w4a4_group).
+
+    products: list of dicts with keys a (bf16 [M, K]), w (codes, scales,
+    global), workspace (uint8 device tensor, at least
+    workspace_bytes(OP_GEMM_W4A4, M, K)), and optionally a_global, out
+    ([M, N] of out_dtype) and reuse_act (multiply what the workspace holds
+    once every activation of the call is quantized).  Returns the outputs."""
+    arr = (GemmProduct * max(1, len(products)))()
+    outs = []
+    for i, p in enumerate(products):
+        a, (c, sc, g), ws = p["a"], p["w"], p["workspace"]
+        ag = p.get("a_global")
+        _need_cuda(a, c, sc, g, ws, ag)
+        if a.dtype != torch.bfloat16 or a.dim() != 2:
+            raise ValueError("a must be a 2-D bfloat16 tensor")
+        M, K = a.shape
+        N = _check_weight(c, sc, K)
+        y = p.get("out")
+        if y is None:
+            y = torch.empty((M, N), dtype=out_dtype, device=a.device)
+        elif y.dtype != out_dtype:
+            raise ValueError("every output must have out_dtype")
+        arr[i] = GemmProduct(a.data_ptr(), None if ag is None else ag.data_ptr(), c.data_ptr(), sc.data_ptr(),
+                             g.data_ptr(), M, N, K, y.data_ptr(),
+                             GEMM_REUSE_ACT if p.get("reuse_act") else GEMM_QUANTIZE_ACT, ws.data_ptr(), ws.numel())
+        outs.append(y)
+    st = lib().nvfp4_gemm_w4a4_group(arr, len(products), _dtype_code(out_dtype), _stream())
+    _check("nvfp4_gemm_w4a4_group", st)
+    return outs
 
 
 def gemm_w4a4_noalloc(a, w_codes, w_scales, w_global, a_global=None, out_dtype=torch.bfloat16, out=None,

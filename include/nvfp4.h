@@ -4,7 +4,8 @@
  *     nvfp4_quantize_4o6 (four-over-six), and nvfp4_dequant;
  *   - W4A16 decode product: nvfp4_gemv_w4a16;
  *   - W4A4 product with per-call activation quantization: nvfp4_gemm_w4a4
- *     (and nvfp4_gemm_w4a4_noalloc, its variant on a fixed device scratch),
+ *     (nvfp4_gemm_w4a4_group for several products in one launch, and
+ *     nvfp4_gemm_w4a4_noalloc, its variant on a fixed device scratch),
  *     with a fused 16-bit low-rank (LoRA) branch: nvfp4_gemm_w4a4_lora, and
  *     on an SVDQuant-smoothed input: nvfp4_gemm_w4a4_svdq;
  *   - calibration of a static activation scale: nvfp4_act_amax,
@@ -228,6 +229,45 @@ int nvfp4_gemm_w4a4(const void* a, const float* a_global, const uint8_t* w_codes
                     const uint8_t* w_scales, const float* w_global,
                     int64_t M, int64_t N, int64_t K, void* y, int y_dtype, int flags,
                     void* workspace, size_t ws_bytes, void* stream);
+
+/* One product of nvfp4_gemm_w4a4_group: the arguments of one
+ * nvfp4_gemm_w4a4 call (y_dtype and stream are the group's). */
+typedef struct {
+  const void* a;              /* [M, K] bf16 (not read with NVFP4_GEMM_REUSE_ACT) */
+  const float* a_global;      /* NULL: dynamic s_gA; else a device fp32 (static s_gA) */
+  const uint8_t* w_codes;     /* [N, K/2] */
+  const uint8_t* w_scales;    /* [N, K/16] */
+  const float* w_global;      /* one device fp32 */
+  int64_t M, N, K;
+  void* y;                    /* [M, N] of the group's y_dtype */
+  int flags;                  /* NVFP4_GEMM_QUANTIZE_ACT or NVFP4_GEMM_REUSE_ACT */
+  void* workspace;            /* >= nvfp4_workspace_bytes(NVFP4_OP_GEMM_W4A4, M, K), 256-byte aligned */
+  size_t ws_bytes;
+} nvfp4_gemm_w4a4_product;
+
+/*
+ * nvfp4_gemm_w4a4_group -- several independent W4A4 products in one launch
+ * per 8 products ("NVFP4 en difusion ...", section 1: a double-stream DiT
+ * block sends image and text tokens through separate weights, so each of its
+ * layers is one product per stream; section 2: the per-call activation
+ * quantization and out = (A s_a)(B s_b)^T of nvfp4_gemm_w4a4).  Each product
+ * gives the same result bit for bit as nvfp4_gemm_w4a4 would without split-K
+ * partials: 256 x 256 tiles of all the products share one grid, so a phase
+ * whose products each leave part of the chip idle fills it.
+ *   products  host array of n descriptors, read during the call only;
+ *             n >= 0 (NVFP4_ERR_SHAPE if negative, NVFP4_ERR_NULL for NULL
+ *             with n > 0); every descriptor is checked as nvfp4_gemm_w4a4
+ *             checks its arguments, before anything is launched
+ *   y_dtype   NVFP4_BF16 or NVFP4_F32, for every product
+ * Order: every product with NVFP4_GEMM_QUANTIZE_ACT first quantizes its
+ * activation into its workspace (in array order), then all the products run;
+ * a product with NVFP4_GEMM_REUSE_ACT multiplies what its workspace holds at
+ * that point, e.g. the activation another product of the same call quantized
+ * into the same workspace (q, k and v sharing one input).  Two products that
+ * quantize must not share a workspace, and no output may overlap an input or
+ * workspace of the call.
+ */
+int nvfp4_gemm_w4a4_group(const nvfp4_gemm_w4a4_product* products, int64_t n, int y_dtype, void* stream);
 
 /*
  * nvfp4_gemm_w4a4_noalloc -- nvfp4_gemm_w4a4 for callers that cannot

@@ -25,14 +25,14 @@ def header_functions():
 def test_library_exports_every_declared_symbol():
     L = nv.lib()
     names = header_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(L, n), n
         assert n in nv.SIGNATURES, n
 
 
 def test_status_strings_and_version():
-    assert nv.lib().nvfp4_version() == 10700
+    assert nv.lib().nvfp4_version() == 10800
     for s in range(11):
         assert nv.status_string(s) and nv.status_string(s) != "unknown status"
     assert nv.status_string(99) == "unknown status"
@@ -233,3 +233,32 @@ def test_gemm_noalloc_validation():
     assert nv.status_string(nv.ERR_SCRATCH).startswith("the call needs more than")
     m = re.search(r"#define NVFP4_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) \* 1024 \* 1024\)", open(HEADER).read())
     assert m and int(m.group(1)) * 1024 * 1024 == nv.NOALLOC_SCRATCH_BYTES
+
+
+def test_gemm_group_validation():
+    """Every product of a group is checked as nvfp4_gemm_w4a4 checks its
+    arguments, before anything is launched; empty products need no launch."""
+    f = nv.lib().nvfp4_gemm_w4a4_group
+    W = nv.workspace_bytes(nv.OP_GEMM_W4A4, 64, 64)
+
+    def prod(a=A16, ag=None, wc=A16, ws=A4, wg=A4, M=64, N=64, K=64, y=A16, flags=0, work=A16 * 16, wsb=W):
+        return nv.GemmProduct(a, ag, wc, ws, wg, M, N, K, y, flags, work, wsb)
+
+    def call(*ps, n=None, dt=nv.BF16):
+        arr = (nv.GemmProduct * max(1, len(ps)))(*ps)
+        return f(arr, len(ps) if n is None else n, dt, None)
+
+    assert f(None, 0, nv.BF16, None) == nv.OK
+    assert f(None, 1, nv.BF16, None) == nv.ERR_NULL
+    assert call(prod(), n=-1) == nv.ERR_SHAPE
+    assert call(prod(), dt=3) == nv.ERR_DTYPE
+    assert call(prod(), prod(a=None)) == nv.ERR_NULL
+    assert call(prod(a=None, flags=nv.GEMM_REUSE_ACT, M=0)) == nv.OK      # reuse: a unused
+    assert call(prod(flags=4)) == nv.ERR_FLAGS
+    assert call(prod(K=24)) == nv.ERR_SHAPE
+    assert call(prod(K=96)) == nv.ERR_UNSUPPORTED
+    assert call(prod(y=A16 + 4)) == nv.ERR_ALIGN
+    assert call(prod(work=A16 * 16 + 16)) == nv.ERR_ALIGN
+    assert call(prod(wsb=W - 1)) == nv.ERR_WORKSPACE
+    assert call(prod(work=None)) == nv.ERR_NULL
+    assert call(prod(M=0), prod(N=0)) == nv.OK

@@ -381,3 +381,102 @@ def test_gemm_maximum_k_256_row_panels():
     pm, pn = pm.reshape(-1), pn.reshape(-1)
     ystar, tau = oracle.dot_w4a4(ac, as_, asg, wc, ws_, sgw, K, pairs=(pm, pn % 256), M=rows.size, N=256)
     assert_within_tau(y[rows[pm], pn], ystar, tau, "max K 256-row panels")
+
+
+def _plain(ab_dev, w, M, N, K, out_dtype, a_global=None):
+    """nvfp4_gemm_w4a4 without split-K room (the grouped products never split)."""
+    ws = torch.empty(nv.gemm_workspace_bytes(M, N, K, split_k=False), dtype=torch.uint8, device=DEV)
+    return host(nv.gemm_w4a4(ab_dev, *w, a_global=a_global, out_dtype=out_dtype, workspace=ws))
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_gemm_group_matches_single_products_and_oracle(out_dtype):
+    """A group of ragged products (one activation quantized once and reused by
+    a second weight through the shared workspace, one with a static scale,
+    partial tiles in M and N, different K): every output bit-identical to its
+    own nvfp4_gemm_w4a4 call and within the oracle's tau (fp32) or bracket
+    (bf16)."""
+    shapes = [(300, 520, 512), (300, 130, 512), (70, 1000, 192), (257, 300, 4096), (1, 64, 64)]
+    prods, refs, checks = [], [], []
+    ws0 = None
+    for i, (M, N, K) in enumerate(shapes):
+        a = inputs.normal_f32((M, K), 400 + (0 if i == 1 else i))
+        a, _ = inputs.with_outlier_columns(a, max(1, K // 100), 410 + (0 if i == 1 else i))
+        ab = inputs.to_bf16_bits(a)
+        w = _quant_weight(inputs.student_t_f32((N, K), 420 + i), oracle.MSE)
+        ag = torch.tensor([0.004], dtype=torch.float32, device=DEV) if i == 2 else None
+        a_dev = dev_bf16(ab)
+        ws = torch.empty(nv.workspace_bytes(nv.OP_GEMM_W4A4, M, K), dtype=torch.uint8, device=DEV)
+        if i == 0:
+            ws0 = ws
+        p = {"a": a_dev, "w": w, "workspace": ws0 if i == 1 else ws, "a_global": ag, "reuse_act": i == 1}
+        prods.append(p)
+        refs.append(_plain(a_dev, w, M, N, K, out_dtype, a_global=ag))
+        checks.append((ab, w, M, N, K, None if ag is None else 0.004))
+    print(f"[case] gemm group of {len(prods)} products, {out_dtype}", flush=True)
+    outs = nv.gemm_w4a4_group(prods, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    for y, ref, (ab, w, M, N, K, ag) in zip(outs, refs, checks):
+        got = host(y)
+        assert np.array_equal(got, ref), (M, N, K)
+        ac, as_, asg = oracle.quantize(inputs.bf16_bits_to_f32(ab), oracle.ABSMAX, sg=ag)
+        oc, os_, og = _oracle_weight(w[0])
+        ystar, tau = oracle.dot_w4a4_matmul(ac, as_, asg, oc, os_, og, K)
+        if out_dtype == torch.float32:
+            assert_within_tau(got.reshape(-1), ystar.reshape(-1), tau.reshape(-1), f"group {M}x{N}x{K}")
+        else:
+            assert_bracket_bf16(got.reshape(-1), ystar.reshape(-1), tau.reshape(-1), f"group {M}x{N}x{K}")
+
+
+def test_gemm_group_more_products_than_one_launch():
+    """11 products (more than the 8 of one launch), each equal to its own call."""
+    prods, refs = [], []
+    for i in range(11):
+        M, N, K = 32 + 37 * i, 64 + 96 * (i % 4), 64 * (1 + i % 3)
+        ab = inputs.to_bf16_bits(inputs.normal_f32((M, K), 500 + i))
+        w = _quant_weight(inputs.student_t_f32((N, K), 520 + i))
+        a_dev = dev_bf16(ab)
+        ws = torch.empty(nv.workspace_bytes(nv.OP_GEMM_W4A4, M, K), dtype=torch.uint8, device=DEV)
+        prods.append({"a": a_dev, "w": w, "workspace": ws})
+        refs.append(_plain(a_dev, w, M, N, K, torch.float32))
+    print("[case] gemm group of 11 products", flush=True)
+    outs = nv.gemm_w4a4_group(prods, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for y, ref in zip(outs, refs):
+        assert np.array_equal(host(y), ref)
+
+
+@pytest.mark.parametrize("phase", ["qkv", "mlp_up", "mlp_down"])
+def test_gemm_group_dit_block_phases_sampled(phase):
+    """The DiT block's phases as the benchmark runs them, image and text
+    streams in one group (q/k/v: 6 products, the image and text q quantizing
+    and k, v reusing; MLP up: 2; MLP down: 2): sampled outputs of every
+    product against the oracle."""
+    a_img, a_txt, h_img, h_txt = inputs.dit_activations()
+    names = {"qkv": ["to_q", "to_k", "to_v"], "mlp_up": ["mlp_up"], "mlp_down": ["mlp_down"]}[phase]
+    prods, checks = [], []
+    for stream, (a, h) in enumerate(((a_img, h_img), (a_txt, h_txt))):
+        act = h if phase == "mlp_down" else a
+        M, K = act.shape
+        a_dev = dev_bf16(act)
+        ws = torch.empty(nv.workspace_bytes(nv.OP_GEMM_W4A4, M, K), dtype=torch.uint8, device=DEV)
+        raw = dict(inputs.dit_weights(stream))
+        for j, name in enumerate(names):
+            w = _quant_weight(raw[name])
+            prods.append({"a": a_dev, "w": w, "workspace": ws, "reuse_act": j > 0})
+            checks.append((act, w, stream, name))
+        del raw
+    print(f"[case] gemm group dit phase {phase}: {len(prods)} products", flush=True)
+    outs = nv.gemm_w4a4_group(prods, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    quantized = {}
+    for y, (act, w, stream, name) in zip(outs, checks):
+        M, K = act.shape
+        if stream not in quantized:
+            quantized[stream] = oracle.quantize(inputs.bf16_bits_to_f32(act), oracle.ABSMAX)
+        ac, as_, asg = quantized[stream]
+        oc, os_, og = _oracle_weight(w[0])
+        N = oc.shape[0]
+        pairs = _sample_pairs(M, N, 400, 600 + stream * 10 + len(name))
+        ystar, tau = oracle.dot_w4a4(ac, as_, asg, oc, os_, og, K, pairs=pairs, M=M, N=N)
+        assert_within_tau(host(y)[pairs[0], pairs[1]], ystar, tau, f"dit {phase} stream{stream} {name}")
