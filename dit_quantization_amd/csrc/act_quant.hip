@@ -25,19 +25,21 @@ namespace nvfp4 {
 // and order-free, so every workgroup gets the same value, equal to what a
 // separate reduction pass would produce.  Called by all 256 threads.
 __device__ __forceinline__ float act_scale_256(const ActScale& s) {
-  static_assert(kMaxAmaxPartials <= 8 * 256, "one batch of loads covers every partial");
+  constexpr int kLoads = (kMaxAmaxPartials + 255) / 256;  // every partial requested in one batch
   __shared__ float red[4];
   float sg;
   if (s.partials == nullptr) {
     sg = *s.src;
   } else {
-    float v[8];
+    float v[kLoads];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < kLoads; ++j) {
       const int i = threadIdx.x + 256 * j;
       v[j] = i < s.np ? s.partials[i] : 0.0f;
     }
-    float m = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+    float m = v[0];
+#pragma unroll
+    for (int j = 1; j < kLoads; ++j) m = fmaxf(m, v[j]);
     m = wave_max(m);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
@@ -100,8 +102,11 @@ hipError_t launch_act_quant_f16(const uint16_t* a, int64_t n_elems, ActScale sg,
                                 hipStream_t stream) {
   int64_t n_half = n_elems / 8;
   if (n_half == 0) return hipSuccess;  // (M = 0 or K = 0 never reach here: the C ABI returns first)
-  int64_t wg = (n_half + 511) / 512;  // two half blocks per lane
-  if (wg > 8192) wg = 8192;
+  // two half blocks per lane; at most 2048 workgroups, each of which reduces
+  // the amax partials first (8192 workgroups measured 1-3 us slower on the
+  // prefill and DiT activations, interleaved runs)
+  int64_t wg = (n_half + 511) / 512;
+  if (wg > 2048) wg = 2048;
   hipLaunchKernelGGL(act_quant_f16_kernel, dim3((unsigned)wg), dim3(256), 0, stream,
                      reinterpret_cast<const u32x4*>(a), n_half, sg, reinterpret_cast<u32x4*>(a_hat));
   return hipGetLastError();

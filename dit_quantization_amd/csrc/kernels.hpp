@@ -7,7 +7,7 @@
 
 namespace nvfp4 {
 
-constexpr int kMaxAmaxPartials = 2048;
+constexpr int kMaxAmaxPartials = 512;
 constexpr int kSweepCandidates = 17;  // static activation scale candidates, E4M3 448 down to 112
 
 int amax_partial_count(int64_t n_elems, bool bf16);
