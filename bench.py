@@ -288,7 +288,7 @@ def main():
 
     # The image and text streams of a double-stream DiT block are independent
     # until the joint attention, which needs both streams' q, k and v; the
-    # MLPs come after it.  Each phase runs the two streams' products on two
+    # MLPs come after it.  A phase can run the two streams' products on two
     # HIP streams (both at the default priority), forked from and joined back
     # into the timed stream.  In the MLP phase the image MLP-up product fills
     # the chip, so the text MLP is queued behind it and runs beside the image
@@ -303,9 +303,7 @@ def main():
         run_img()
         main.wait_stream(side)
 
-    def dit_phases(img, txt):
-        """img, txt: (q/k/v products, MLP up, MLP down) of one stream each."""
-        two_streams(img[0], txt[0])
+    def mlp_two_streams(img, txt):
         main = torch.cuda.current_stream()
         img[1]()
         side.wait_stream(main)
@@ -314,6 +312,11 @@ def main():
             txt[2]()
         img[2]()
         main.wait_stream(side)
+
+    def dit_phases(img, txt):
+        """img, txt: (q/k/v products, MLP up, MLP down) of one stream each."""
+        two_streams(img[0], txt[0])
+        mlp_two_streams(img, txt)
 
     if "gemm" in phases or "dit" in phases:
         log("[setup] dit block")
@@ -350,24 +353,9 @@ def main():
 
         dit_img, dit_txt = dit_stream(*dit_calls[0]), dit_stream(*dit_calls[1])
 
-        def dit_block():
-            dit_phases(dit_img, dit_txt)
-
-        capture("gemm_dit_block", dit_block, flops=dit_flops)
-
-        # The linears of consecutive blocks / denoising steps back to back,
-        # with no idle gap between blocks (reported beside the isolated block,
-        # outside value).
-        def dit_blocks_sustained():
-            for _ in range(DIT_SUSTAINED_BLOCKS):
-                dit_phases(dit_img, dit_txt)
-
-        capture("dit_block_sustained", dit_blocks_sustained, flops=DIT_SUSTAINED_BLOCKS * dit_flops,
-                calls=DIT_SUSTAINED_BLOCKS)
-
-        # The same block with each phase's image and text products in one
-        # grouped launch (nvfp4_gemm_w4a4_group) on one stream: q/k/v of
-        # both streams (6 products), MLP up (2), MLP down (2).
+        # Grouped launches (nvfp4_gemm_w4a4_group): one phase's image and text
+        # products in one grid of 256x256 tiles, both activations quantized
+        # first (k and v reuse q's quantized input).
         def group_phase(names, act):
             prods = []
             for ad, hd, w, ws_a, ws_h, outs in dit_calls:
@@ -378,6 +366,32 @@ def main():
 
         grouped = [group_phase(["to_q", "to_k", "to_v"], "a"), group_phase(["mlp_up"], "a"),
                    group_phase(["mlp_down"], "h")]
+
+        # The block: the six q/k/v products of both streams as one grouped
+        # launch (648 tiles), then the MLPs on two HIP streams.
+        def dit_block():
+            nv.gemm_w4a4_group(grouped[0])
+            mlp_two_streams(dit_img, dit_txt)
+
+        capture("gemm_dit_block", dit_block, flops=dit_flops)
+
+        # The linears of consecutive blocks / denoising steps back to back,
+        # with no idle gap between blocks (reported beside the isolated block,
+        # outside value).
+        def dit_blocks_sustained():
+            for _ in range(DIT_SUSTAINED_BLOCKS):
+                dit_block()
+
+        capture("dit_block_sustained", dit_blocks_sustained, flops=DIT_SUSTAINED_BLOCKS * dit_flops,
+                calls=DIT_SUSTAINED_BLOCKS)
+
+        # Two other schedules of the same products, reported beside it: every
+        # phase on two HIP streams (q/k/v too), and every phase as one grouped
+        # launch on one stream.
+        def dit_block_two_streams():
+            dit_phases(dit_img, dit_txt)
+
+        capture("dit_block_two_streams", dit_block_two_streams, flops=dit_flops)
 
         def dit_block_grouped():
             for prods in grouped:
@@ -564,8 +578,8 @@ def main():
     family = {"quantize_mse": "mse", "quantize_4o6": "mse", "quantize_absmax_pass": "absmax",
               "quantize_absmax_dynamic": "absmax"}
     share = {}
-    gemm_family = ("dit_block_sustained", "dit_block_grouped", "lora_dit_block", "svdq_dit_block",
-                   "static_prefill_gate")
+    gemm_family = ("dit_block_sustained", "dit_block_two_streams", "dit_block_grouped", "lora_dit_block",
+                   "svdq_dit_block", "static_prefill_gate")
     for k in names:
         f = family.get(k, "gemm" if k.startswith("gemm_") or k in gemm_family else "gemv" if k.startswith("gemv_")
                        else k)
