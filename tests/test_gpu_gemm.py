@@ -480,3 +480,33 @@ def test_gemm_group_dit_block_phases_sampled(phase):
         pairs = _sample_pairs(M, N, 400, 600 + stream * 10 + len(name))
         ystar, tau = oracle.dot_w4a4(ac, as_, asg, oc, os_, og, K, pairs=pairs, M=M, N=N)
         assert_within_tau(host(y)[pairs[0], pairs[1]], ystar, tau, f"dit {phase} stream{stream} {name}")
+
+
+def test_gemv_splitk_independent_of_workspace_contents():
+    """The split-K ranges of the M > 4 decode product meet in the workspace: a
+    workspace full of random bytes, and one left by split calls of other
+    shapes, give the same bits as a zeroed one, and the result stays within
+    tau of the oracle."""
+    N, K, M = 1000, 16384, 16
+    w = inputs.student_t_f32((N, K), 77)
+    xb = inputs.gemv_x(K, M)
+    oc, os_, og = oracle.quantize(w, oracle.ABSMAX)
+    c, s, g = torch.from_numpy(oc).to(DEV), torch.from_numpy(os_).to(DEV), torch.tensor([og], device=DEV)
+    xd = dev_bf16(xb)
+    wsb = nv.workspace_bytes(nv.OP_GEMV_W4A16, M, N)
+    assert wsb > 0
+    print(f"[case] gemv split-K workspace contents N={N} K={K} M={M}", flush=True)
+    zero = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    ref = host(nv.gemv_w4a16(xd, c, s, g, out_dtype=torch.float32, workspace=zero))
+    ystar, tau = oracle.dot_w4a16(inputs.bf16_bits_to_f32(xb), oc, os_, og)
+    assert_within_tau(ref.reshape(-1), ystar, tau, "split fp32")
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    noisy = torch.randint(0, 256, (wsb,), dtype=torch.uint8, generator=gen).to(DEV)
+    assert np.array_equal(host(nv.gemv_w4a16(xd, c, s, g, out_dtype=torch.float32, workspace=noisy)), ref)
+    # the same workspace after split calls of other shapes (other row blocks and range counts)
+    for n2, k2, m2 in ((300, 8320, 5), (64, 8192, 16), (1000, 16384, 8)):
+        x2 = dev_bf16(inputs.gemv_x(k2, m2))
+        c2, s2, g2 = nv.quantize_absmax(torch.randn(n2, k2, device=DEV) * 0.02)
+        nv.gemv_w4a16(x2, c2, s2, g2, workspace=noisy)
+    for _ in range(3):
+        assert np.array_equal(host(nv.gemv_w4a16(xd, c, s, g, out_dtype=torch.float32, workspace=noisy)), ref)
