@@ -21,7 +21,7 @@ namespace {
 
 using namespace nvfp4;
 
-constexpr int kVersion = 1 * 10000 + 8 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 8 * 100 + 1;
 static_assert(kSweepCandidates == NVFP4_SWEEP_CANDIDATES, "candidate count of the activation scale sweep");
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -147,9 +147,12 @@ int gemm_check(const void* a, const float* a_global, const uint8_t* w_codes, con
                size_t ws_bytes, bool use_scratch) {
   const bool reuse = (flags & NVFP4_GEMM_REUSE_ACT) != 0;
   const bool lora = rank != 0;
-  if ((!a && !reuse) || !w_codes || !w_scales || !w_global || !y || (!workspace && !use_scratch))
+  // an empty product (M = 0 or N = 0) reads no pointer: only its sizes and
+  // flags are checked
+  const bool empty = M == 0 || N == 0;
+  if (!empty && ((!a && !reuse) || !w_codes || !w_scales || !w_global || !y || (!workspace && !use_scratch)))
     return NVFP4_ERR_NULL;
-  if (lora && ((!lora_down && !reuse) || !lora_up)) return NVFP4_ERR_NULL;
+  if (!empty && lora && ((!lora_down && !reuse) || !lora_up)) return NVFP4_ERR_NULL;
   if (flags & ~1) return NVFP4_ERR_FLAGS;
   if (y_dtype != NVFP4_F32 && y_dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
   if (M < 0 || N < 0 || K < 0 || rank < 0 || !mul_ok(M, K) || !mul_ok(N, K) || !mul_ok(M, N)) return NVFP4_ERR_SHAPE;
@@ -160,6 +163,7 @@ int gemm_check(const void* a, const float* a_global, const uint8_t* w_codes, con
   if (K % 64 != 0 || K == 0 || M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > kMaxGemmK)
     return NVFP4_ERR_UNSUPPORTED;
   if (lora && (rank % 16 != 0 || rank > kMaxLoraRank)) return NVFP4_ERR_UNSUPPORTED;
+  if (empty) return NVFP4_OK;
   if ((!reuse && !aligned(a, 16)) || !aligned(w_codes, 16) || !aligned(w_scales, 4) || !aligned(w_global, 4) ||
       (a_global && !aligned(a_global, 4)) || !aligned(y, 16) || (!use_scratch && !aligned(workspace, 256)))
     return NVFP4_ERR_ALIGN;
@@ -308,13 +312,14 @@ int nvfp4_quantize_4o6(const void* x, int x_dtype, int64_t rows, int64_t cols, u
 
 int nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const float* global_scale, int64_t rows,
                   int64_t cols, void* out, int out_dtype, void* stream) {
-  if (!codes || !scales || !global_scale || !out) return NVFP4_ERR_NULL;
+  const bool empty = rows == 0 || cols == 0;  // reads no pointer
+  if (!empty && (!codes || !scales || !global_scale || !out)) return NVFP4_ERR_NULL;
   if (out_dtype != NVFP4_F32 && out_dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
   if (rows < 0 || cols < 0 || !mul_ok(rows, cols)) return NVFP4_ERR_SHAPE;
   if (cols % 16 != 0) return NVFP4_ERR_SHAPE;
   if (cols % 32 != 0) return NVFP4_ERR_UNSUPPORTED;
+  if (empty) return NVFP4_OK;
   if (!aligned(codes, 4) || !aligned(global_scale, 4) || !aligned(out, 16)) return NVFP4_ERR_ALIGN;
-  if (rows == 0 || cols == 0) return NVFP4_OK;
   if (const int st = stream_status(reinterpret_cast<hipStream_t>(stream)); st != NVFP4_OK) return st;
   clear_error();
   return launch_status(launch_dequant(codes, scales, global_scale, rows * cols, out, out_dtype == NVFP4_BF16,
@@ -324,16 +329,17 @@ int nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const float* glob
 int nvfp4_gemv_w4a16(const void* x, const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
                      int64_t M, int64_t N, int64_t K, void* y, int y_dtype, void* workspace, size_t ws_bytes,
                      void* stream) {
-  if (!x || !w_codes || !w_scales || !w_global || !y) return NVFP4_ERR_NULL;
+  const bool empty = M == 0 || N == 0;  // reads no pointer
+  if (!empty && (!x || !w_codes || !w_scales || !w_global || !y)) return NVFP4_ERR_NULL;
   if (y_dtype != NVFP4_F32 && y_dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
   if (M < 0 || N < 0 || K < 0 || !mul_ok(M, K) || !mul_ok(N, K) || !mul_ok(M, N)) return NVFP4_ERR_SHAPE;
   if (K % 16 != 0) return NVFP4_ERR_SHAPE;
   if (K % 32 != 0 || M > 16 || K > (int64_t)1 << 24 || N > (int64_t)1 << 30) return NVFP4_ERR_UNSUPPORTED;
+  if (empty) return NVFP4_OK;
   if (!aligned(x, 16) || !aligned(w_codes, 16) || !aligned(w_scales, 4) || !aligned(w_global, 4) ||
       !aligned(y, 4))
     return NVFP4_ERR_ALIGN;
   if (workspace && !aligned(workspace, 256)) return NVFP4_ERR_ALIGN;
-  if (M == 0 || N == 0) return NVFP4_OK;
   if (K == 0) return NVFP4_ERR_UNSUPPORTED;
   // Split-K partial sums when the workspace holds them.
   const int splits = gemv_splits(M, N, K);

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert nv.lib().nvfp4_version() == 10800
+    assert nv.lib().nvfp4_version() == 10801
     for s in range(11):
         assert nv.status_string(s) and nv.status_string(s) != "unknown status"
     assert nv.status_string(99) == "unknown status"
@@ -262,3 +262,30 @@ def test_gemm_group_validation():
     assert call(prod(wsb=W - 1)) == nv.ERR_WORKSPACE
     assert call(prod(work=None)) == nv.ERR_NULL
     assert call(prod(M=0), prod(N=0)) == nv.OK
+
+
+def test_empty_products_accept_null_pointers():
+    """A product or dequantization with an empty output reads no pointer, so
+    NULL ones are accepted (torch's zero-element tensors have NULL data
+    pointers); sizes, dtypes and flags are still checked."""
+    L = nv.lib()
+    R = nv.GEMM_REUSE_ACT
+    assert L.nvfp4_gemv_w4a16(None, None, None, None, 0, 64, 64, None, nv.BF16, None, 0, None) == nv.OK
+    assert L.nvfp4_gemv_w4a16(None, None, None, None, 4, 0, 64, None, nv.BF16, None, 0, None) == nv.OK
+    assert L.nvfp4_gemv_w4a16(None, None, None, None, 0, 64, 40, None, nv.BF16, None, 0, None) == nv.ERR_SHAPE
+    assert L.nvfp4_gemv_w4a16(None, None, None, None, 0, 64, 64, None, 7, None, 0, None) == nv.ERR_DTYPE
+    assert L.nvfp4_gemm_w4a4(None, None, None, None, None, 0, 64, 64, None, nv.BF16, 0, None, 0, None) == nv.OK
+    assert L.nvfp4_gemm_w4a4(None, None, None, None, None, 64, 0, 64, None, nv.F32, R, None, 0, None) == nv.OK
+    assert L.nvfp4_gemm_w4a4(None, None, None, None, None, 0, 64, 64, None, nv.BF16, 4, None, 0, None) == nv.ERR_FLAGS
+    assert L.nvfp4_gemm_w4a4(None, None, None, None, None, 0, 64, 96, None, nv.BF16, 0, None, 0, None) == \
+        nv.ERR_UNSUPPORTED
+    assert L.nvfp4_gemm_w4a4_noalloc(None, None, None, None, None, 0, 64, 64, None, nv.BF16, 0, None) == nv.OK
+    assert L.nvfp4_gemm_w4a4_lora(None, None, None, None, None, None, None, 32, 0, 64, 64, None, nv.BF16, 0, None,
+                                  0, None) == nv.OK
+    assert L.nvfp4_dequant(None, None, None, 0, 64, None, nv.BF16, None) == nv.OK
+    assert L.nvfp4_dequant(None, None, None, 4, 0, None, nv.F32, None) == nv.OK
+    assert L.nvfp4_dequant(None, None, None, 4, 64, None, nv.F32, None) == nv.ERR_NULL
+    prods = (nv.GemmProduct * 2)(nv.GemmProduct(None, None, None, None, None, 0, 64, 64, None, 0, None, 0),
+                                 nv.GemmProduct(None, None, None, None, None, 64, 0, 64, None, R, None, 0))
+    assert L.nvfp4_gemm_w4a4_group(prods, 2, nv.BF16, None) == nv.OK
+

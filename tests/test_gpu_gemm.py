@@ -510,3 +510,42 @@ def test_gemv_splitk_independent_of_workspace_contents():
         nv.gemv_w4a16(x2, c2, s2, g2, workspace=noisy)
     for _ in range(3):
         assert np.array_equal(host(nv.gemv_w4a16(xd, c, s, g, out_dtype=torch.float32, workspace=noisy)), ref)
+
+
+def test_gemm_group_with_empty_products():
+    """Empty products (M = 0 or N = 0) in a group launch nothing and leave the
+    others' results unchanged."""
+    M, N, K = 130, 200, 256
+    ab = inputs.to_bf16_bits(inputs.normal_f32((M, K), 640))
+    w = _quant_weight(inputs.student_t_f32((N, K), 641))
+    a_dev = dev_bf16(ab)
+    ws = torch.empty(nv.workspace_bytes(nv.OP_GEMM_W4A4, M, K), dtype=torch.uint8, device=DEV)
+    ref = _plain(a_dev, w, M, N, K, torch.float32)
+    empty_a = torch.empty((0, K), dtype=torch.bfloat16, device=DEV)
+    ws0 = torch.empty(256, dtype=torch.uint8, device=DEV)
+    w0 = (torch.empty((0, K // 2), dtype=torch.uint8, device=DEV), torch.empty((0, K // 16), dtype=torch.uint8,
+                                                                                  device=DEV), w[2])
+    print("[case] gemm group with empty products", flush=True)
+    outs = nv.gemm_w4a4_group([{"a": empty_a, "w": w, "workspace": ws0},
+                               {"a": a_dev, "w": w, "workspace": ws},
+                               {"a": a_dev, "w": w0, "workspace": ws, "reuse_act": True}], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert outs[0].shape == (0, N) and outs[2].shape == (M, 0)
+    assert np.array_equal(host(outs[1]), ref)
+
+
+def test_empty_calls_through_the_binding():
+    """Zero-row activations and zero-row weights (torch's zero-element tensors
+    have NULL data pointers) give empty outputs without an error."""
+    K = 256
+    c, s, g = _quant_weight(inputs.student_t_f32((64, K), 650))
+    x0 = torch.empty((0, K), dtype=torch.bfloat16, device=DEV)
+    print("[case] empty calls", flush=True)
+    assert nv.gemv_w4a16(x0, c, s, g).shape == (0, 64)
+    assert nv.gemm_w4a4(x0, c, s, g).shape == (0, 64)
+    c0 = torch.empty((0, K // 2), dtype=torch.uint8, device=DEV)
+    s0 = torch.empty((0, K // 16), dtype=torch.uint8, device=DEV)
+    x = dev_bf16(inputs.to_bf16_bits(inputs.normal_f32((3, K), 651)))
+    assert nv.gemv_w4a16(x, c0, s0, g).shape == (3, 0)
+    assert nv.gemm_w4a4(x, c0, s0, g).shape == (3, 0)
+    torch.cuda.synchronize()
