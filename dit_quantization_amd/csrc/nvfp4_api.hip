@@ -76,13 +76,17 @@ int stream_status(hipStream_t s) {
 
 int validate_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, const uint8_t* codes,
                       const uint8_t* scales, const float* gs, int flags, const void* ws, size_t ws_bytes) {
-  if (!x || !codes || !scales || !gs) return NVFP4_ERR_NULL;
+  // an empty tensor (rows = 0 or cols = 0) reads no element: x, codes and
+  // scales may be NULL; a computed s_g (1.0) is still written
+  const bool empty = rows == 0 || cols == 0;
+  const bool compute = (flags & NVFP4_GLOBAL_GIVEN) == 0;
+  if ((!empty && (!x || !codes || !scales)) || ((!empty || compute) && !gs)) return NVFP4_ERR_NULL;
   if (x_dtype != NVFP4_F32 && x_dtype != NVFP4_BF16) return NVFP4_ERR_DTYPE;
   if (flags & ~1) return NVFP4_ERR_FLAGS;
   if (rows < 0 || cols < 0 || !mul_ok(rows, cols)) return NVFP4_ERR_SHAPE;
   if (cols % 16 != 0) return NVFP4_ERR_SHAPE;
   if (cols % 32 != 0) return NVFP4_ERR_UNSUPPORTED;
-  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(gs, 4)) return NVFP4_ERR_ALIGN;
+  if ((!empty && (!aligned(x, 16) || !aligned(codes, 8))) || !aligned(gs, 4)) return NVFP4_ERR_ALIGN;
   if ((flags & NVFP4_GLOBAL_GIVEN) == 0) {
     if (!ws) return NVFP4_ERR_WORKSPACE;
     if (!aligned(ws, 16)) return NVFP4_ERR_ALIGN;

@@ -51,8 +51,10 @@
  *   - a product or dequantization with an empty output (M = 0 or N = 0;
  *     rows = 0 or cols = 0) launches nothing and reads none of its
  *     pointers, which may then be NULL (its sizes, dtypes and flags are
- *     still checked); the quantizers and calibration calls always need
- *     their pointers;
+ *     still checked); a quantizer given an empty tensor takes NULL x, codes
+ *     and scales (with NVFP4_GLOBAL_COMPUTE it still writes s_g = 1.0, so
+ *     global_scale and the workspace are needed); the calibration calls
+ *     always need their pointers;
  *   - the fast path requires cols (K) % 32 == 0 and 16-byte aligned
  *     pointers (4-byte for scales, global scale and 1-row outputs);
  *     otherwise NVFP4_ERR_UNSUPPORTED / NVFP4_ERR_ALIGN is returned;

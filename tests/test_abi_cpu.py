@@ -288,4 +288,11 @@ def test_empty_products_accept_null_pointers():
     prods = (nv.GemmProduct * 2)(nv.GemmProduct(None, None, None, None, None, 0, 64, 64, None, 0, None, 0),
                                  nv.GemmProduct(None, None, None, None, None, 64, 0, 64, None, R, None, 0))
     assert L.nvfp4_gemm_w4a4_group(prods, 2, nv.BF16, None) == nv.OK
+    # quantizers: an empty tensor needs no element pointers; a computed s_g is still written
+    G = nv.GLOBAL_GIVEN
+    assert L.nvfp4_quantize_absmax(None, nv.F32, 0, 64, None, None, None, G, None, 0, None) == nv.OK
+    assert L.nvfp4_quantize_mse(None, nv.BF16, 8, 0, None, None, None, G, None, 0, None) == nv.OK
+    assert L.nvfp4_quantize_4o6(None, nv.F32, 0, 64, None, None, None, 0, None, 0, None) == nv.ERR_NULL
+    assert L.nvfp4_quantize_absmax(None, nv.F32, 0, 64, None, None, None, 0, None, 0, None) == nv.ERR_NULL
+    assert L.nvfp4_quantize_absmax(None, nv.F32, 4, 64, None, None, A4, G, None, 0, None) == nv.ERR_NULL
 

@@ -154,3 +154,15 @@ def test_quantize_absmax_unaligned_scales(offset, dtype):
     assert np.array_equal(host(scales), os_)
     b = host(buf)
     assert np.all(b[:offset] == 0xEE) and np.all(b[offset + rows * cols // 16:] == 0xEE)   # nothing written outside
+
+
+def test_quantize_empty_tensor():
+    """An empty tensor quantizes to empty codes and scales; a computed tensor
+    scale is 1.0 (zero amax), a given one is left as it is."""
+    print("[case] quantize empty tensor", flush=True)
+    for fn in (nv.quantize_absmax, nv.quantize_mse, nv.quantize_4o6):
+        c, s, g = fn(torch.empty((0, 64), dtype=torch.float32, device="cuda:0"))
+        assert c.shape == (0, 32) and s.shape == (0, 4) and float(g.item()) == 1.0
+        c, s, g = fn(torch.empty((3, 0), dtype=torch.bfloat16, device="cuda:0"),
+                     global_scale=torch.tensor([0.25], device="cuda:0"))
+        assert c.shape == (3, 0) and s.shape == (3, 0) and float(g.item()) == 0.25
