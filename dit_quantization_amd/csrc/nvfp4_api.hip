@@ -166,6 +166,10 @@ int gemm_check(const void* a, const float* a_global, const uint8_t* w_codes, con
   static_assert((uint64_t)256 * ((uint64_t)1 << 22) * 2 <= ((uint64_t)1 << 31), "panel bytes fit 32 bits");
   if (K % 64 != 0 || K == 0 || M > (int64_t)1 << 30 || N > (int64_t)1 << 30 || K > kMaxGemmK)
     return NVFP4_ERR_UNSUPPORTED;
+  // at most 2^27 output tiles of 128 x 128 (times up to 8 K ranges), so every
+  // grid and tile index fits 32 bits (an output that large, 2^41 elements,
+  // would not fit in device memory anyway)
+  if (((M + 127) / 128) * ((N + 127) / 128) > ((int64_t)1 << 27)) return NVFP4_ERR_UNSUPPORTED;
   if (lora && (rank % 16 != 0 || rank > kMaxLoraRank)) return NVFP4_ERR_UNSUPPORTED;
   if (empty) return NVFP4_OK;
   if ((!reuse && !aligned(a, 16)) || !aligned(w_codes, 16) || !aligned(w_scales, 4) || !aligned(w_global, 4) ||
@@ -396,8 +400,7 @@ int nvfp4_gemm_w4a4_group(const nvfp4_gemm_w4a4_product* products, int64_t n, in
   for (int64_t i = 0; i < n; ++i) {
     const nvfp4_gemm_w4a4_product& p = products[i];
     if (p.M == 0 || p.N == 0) continue;
-    const int64_t tiles = gemm_group_tiles(p.M, p.N);
-    if (tiles > INT32_MAX) return NVFP4_ERR_UNSUPPORTED;  // more tiles than one grid holds
+    const int64_t tiles = gemm_group_tiles(p.M, p.N);  // < 2^27 (checked above)
     if (g.n == kMaxGemmGroup || (int64_t)g.tile_begin[g.n] + tiles > INT32_MAX) {
       if (flush() != hipSuccess) return NVFP4_ERR_LAUNCH;
     }

@@ -209,7 +209,8 @@ int nvfp4_gemv_w4a16(const void* x, const uint8_t* w_codes, const uint8_t* w_sca
  *   y        [M, N] of y_dtype (NVFP4_BF16 or NVFP4_F32)
  *   K % 64 == 0 (one K step of the kernel; all configured shapes qualify)
  *   and K <= 2^22 (32-bit addressing of a 256-row operand panel),
- *   otherwise NVFP4_ERR_UNSUPPORTED; M, N <= 2^30.
+ *   otherwise NVFP4_ERR_UNSUPPORTED; M, N <= 2^30 and at most 2^27 output
+ *   tiles of 128 x 128 (M N up to about 2^41), else NVFP4_ERR_UNSUPPORTED.
  *   workspace >= nvfp4_workspace_bytes(NVFP4_OP_GEMM_W4A4, M, K) bytes,
  *            256-byte aligned.  On return it holds, at fixed offsets:
  *              [0, 4)       s_gA (fp32)

@@ -296,3 +296,18 @@ def test_empty_products_accept_null_pointers():
     assert L.nvfp4_quantize_absmax(None, nv.F32, 0, 64, None, None, None, 0, None, 0, None) == nv.ERR_NULL
     assert L.nvfp4_quantize_absmax(None, nv.F32, 4, 64, None, None, A4, G, None, 0, None) == nv.ERR_NULL
 
+
+def test_gemm_output_tile_limit():
+    """At most 2^27 output tiles of 128 x 128 (grid and tile indices stay
+    within 32 bits), checked before anything is launched, also per product of
+    a group."""
+    L = nv.lib()
+    W = 1 << 40
+    big = 1 << 30
+    assert L.nvfp4_gemm_w4a4(A16, None, A16, A16, A4, big, big, 64, A16, nv.BF16, 0, A16, W, None) == \
+        nv.ERR_UNSUPPORTED
+    assert L.nvfp4_gemm_w4a4(A16, None, A16, A16, A4, 1 << 21, (1 << 20) + 128, 64, A16, nv.BF16, 0, A16, W, None) == \
+        nv.ERR_UNSUPPORTED
+    prods = (nv.GemmProduct * 1)(nv.GemmProduct(A16, None, A16, A16, A4, big, big, 64, A16, 0, A16, W))
+    assert L.nvfp4_gemm_w4a4_group(prods, 1, nv.BF16, None) == nv.ERR_UNSUPPORTED
+
